@@ -1,0 +1,87 @@
+"""Pure-Python brute force of sink attention, written from the definition
+(Perplexity blog "GPT-OSS on day 0", section "Kernels for GPT-OSS > Sink
+attention": the per-head sink is one more term of the softmax denominator).
+
+Independent of ``oracle/``: its own gather, its own causal/window rule, no
+max subtraction, ``math.fsum`` for every sum.  Used only on tiny inputs to pin
+the oracle.  ``mp_attention`` repeats it in 50-digit mpmath arithmetic.
+"""
+
+import math
+
+
+def _key_rows(kvspec, b, g):
+    """List of (k_row, v_row) of request b, KV head g, in logical order."""
+    if kvspec["paged"]:
+        rows = []
+        start = kvspec["page_indptr"][b]
+        for j in range(kvspec["kv_len"][b]):
+            page = kvspec["page_indices"][start + j // kvspec["page_size"]]
+            slot = j % kvspec["page_size"]
+            rows.append((list(kvspec["k"][page][g][slot]), list(kvspec["v"][page][g][slot])))
+        return rows
+    lo, hi = kvspec["kv_indptr"][b], kvspec["kv_indptr"][b + 1]
+    return [(list(kvspec["k"][r][g]), list(kvspec["v"][r][g])) for r in range(lo, hi)]
+
+
+def brute_attention(q, qo_indptr, kvspec, sinks, scale, window, num_kv_heads):
+    """Returns (out, lse) as nested lists: out[row][head][dim], lse[row][head]."""
+    n_heads = len(sinks)
+    group = n_heads // num_kv_heads
+    out, lse = [], []
+    for b in range(len(qo_indptr) - 1):
+        n_q = qo_indptr[b + 1] - qo_indptr[b]
+        for t in range(n_q):
+            row = qo_indptr[b] + t
+            o_row, l_row = [], []
+            for h in range(n_heads):
+                g = h // group
+                keys = _key_rows(kvspec, b, g)
+                n_k = len(keys)
+                pos = n_k - n_q + t
+                first = max(0, pos - window + 1) if window > 0 else 0
+                weights, vals = [], []
+                for j in range(first, pos + 1):
+                    kr, vr = keys[j]
+                    s = scale * math.fsum(a * c for a, c in zip(q[row][h], kr))
+                    weights.append(math.exp(s))
+                    vals.append(vr)
+                z = math.fsum(weights + [math.exp(sinks[h])])
+                d = len(q[row][h])
+                o_row.append([math.fsum(w * v[i] for w, v in zip(weights, vals)) / z for i in range(d)])
+                l_row.append(math.log(z))
+            out.append(o_row)
+            lse.append(l_row)
+    return out, lse
+
+
+def mp_attention(q, qo_indptr, kvspec, sinks, scale, window, num_kv_heads, dps=50):
+    import mpmath
+    mpmath.mp.dps = dps
+    n_heads = len(sinks)
+    group = n_heads // num_kv_heads
+    out, lse = [], []
+    for b in range(len(qo_indptr) - 1):
+        n_q = qo_indptr[b + 1] - qo_indptr[b]
+        for t in range(n_q):
+            row = qo_indptr[b] + t
+            o_row, l_row = [], []
+            for h in range(n_heads):
+                g = h // group
+                keys = _key_rows(kvspec, b, g)
+                n_k = len(keys)
+                pos = n_k - n_q + t
+                first = max(0, pos - window + 1) if window > 0 else 0
+                z = mpmath.exp(mpmath.mpf(sinks[h])) if sinks[h] != -math.inf else mpmath.mpf(0)
+                acc = [mpmath.mpf(0)] * len(q[row][h])
+                for j in range(first, pos + 1):
+                    kr, vr = keys[j]
+                    s = mpmath.mpf(scale) * mpmath.fsum(mpmath.mpf(a) * mpmath.mpf(c) for a, c in zip(q[row][h], kr))
+                    e = mpmath.exp(s)
+                    z += e
+                    acc = [a + e * mpmath.mpf(v) for a, v in zip(acc, vr)]
+                o_row.append([float(a / z) for a in acc])
+                l_row.append(float(mpmath.log(z)))
+            out.append(o_row)
+            lse.append(l_row)
+    return out, lse

@@ -1,0 +1,466 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Sources: Perplexity blog "GPT-OSS on day 0" (French rendering "GPT-OSS au
+jour J"), section "Kernels for GPT-OSS > Sink attention" (extra per-head term
+in the softmax; streaming state starts at m = sink, d = 1; sink in the first
+KV block only) and section "GPT-OSS on Hopper" (GQA with one pretrained sink
+per head).
+
+Kinds of pin: hand-worked examples (tests/golden), pure-Python and 50-digit
+brute force, closed forms built on library attention (torch SDPA in fp64,
+scipy logsumexp), invariants (mass, split == unsplit with a negative
+control, GQA == repeated-KV MHA, page permutation), limits (sink -> +inf),
+and planted mistakes that the pins must catch.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.sink_attention as sa
+from tests import _loops
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def _sink_value(expr):
+    expr = str(expr).strip()
+    if expr.startswith("ln "):
+        return math.log(float(expr[3:]))
+    return float(expr)
+
+
+def _lse_value(spec):
+    return spec["const"] + math.log(spec["ln"])
+
+
+# ----------------------------------------------------------------------------
+# tiny random problems
+# ----------------------------------------------------------------------------
+
+def _tiny_problem(rng, paged, batch=None, hq=None, hkv=None, d=None, max_len=9, page_size=4,
+                  qo_mode="mixed", sink_kind="normal"):
+    batch = batch or int(rng.integers(1, 3))
+    hkv = hkv or int(rng.integers(1, 3))
+    hq = hq or hkv * int(rng.integers(1, 3))
+    d = d or int(rng.integers(1, 5))
+    kv_len = rng.integers(1, max_len + 1, size=batch)
+    if qo_mode == "decode":
+        qo_len = np.ones(batch, dtype=np.int64)
+    else:
+        qo_len = np.array([int(rng.integers(1, l + 1)) for l in kv_len])
+    qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int64)
+    q = rng.normal(0, 1, size=(int(qo_len.sum()), hq, d))
+    if sink_kind == "normal":
+        sinks = rng.normal(0, 2, size=hq)
+    elif sink_kind == "mixed":
+        sinks = rng.normal(0, 2, size=hq)
+        sinks[0] = -np.inf
+    else:
+        sinks = np.full(hq, float(sink_kind))
+    if paged:
+        n_pages = (kv_len + page_size - 1) // page_size
+        page_indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int64)
+        pool = int(page_indptr[-1]) + 2
+        perm = rng.permutation(pool)
+        page_indices = perm[: page_indptr[-1]]
+        k = rng.normal(0, 1, size=(pool, hkv, page_size, d))
+        v = rng.normal(0, 1, size=(pool, hkv, page_size, d))
+        kv = oracle.KVCache(k=k, v=v, kv_indptr=page_indptr, paged=True, page_indices=page_indices,
+                            kv_len=kv_len, page_size=page_size)
+        spec = dict(paged=True, k=k.tolist(), v=v.tolist(), page_indptr=page_indptr.tolist(),
+                    page_indices=page_indices.tolist(), kv_len=kv_len.tolist(), page_size=page_size)
+    else:
+        kv_indptr = np.concatenate([[0], np.cumsum(kv_len)]).astype(np.int64)
+        k = rng.normal(0, 1, size=(int(kv_indptr[-1]), hkv, d))
+        v = rng.normal(0, 1, size=(int(kv_indptr[-1]), hkv, d))
+        kv = oracle.KVCache(k=k, v=v, kv_indptr=kv_indptr)
+        spec = dict(paged=False, k=k.tolist(), v=v.tolist(), kv_indptr=kv_indptr.tolist())
+    window = int(rng.choice([0, 0, 1, 2, 3, max_len + 3]))
+    scale = float(rng.choice([0.125, 0.5, 1.0]))
+    return dict(q=q, qo_indptr=qo_indptr, kv=kv, spec=spec, sinks=sinks, scale=scale,
+                window=window, hkv=hkv)
+
+
+def _brute(p, fn=_loops.brute_attention):
+    return fn(p["q"].tolist(), p["qo_indptr"].tolist(), p["spec"], p["sinks"].tolist(),
+              p["scale"], p["window"], p["hkv"])
+
+
+def _oracle(p, **kw):
+    return oracle.sink_attention_ref(p["q"], p["qo_indptr"], p["kv"], p["sinks"], p["scale"],
+                                     p["window"], **kw)
+
+
+# ----------------------------------------------------------------------------
+# hand-worked examples
+# ----------------------------------------------------------------------------
+
+def _golden():
+    with open(GOLDEN) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("case", _golden()["cases"], ids=lambda c: c["name"])
+def test_golden_hand_worked(case):
+    q = np.array(case["q"], dtype=np.float64)[:, None, :]
+    k = np.array(case["k"], dtype=np.float64)[:, None, :]
+    v = np.array(case["v"], dtype=np.float64)[:, None, :]
+    kv = oracle.KVCache(k=k, v=v, kv_indptr=np.array([0, len(k)]))
+    sink = np.array([_sink_value(case["sink"])])
+    out, lse = oracle.sink_attention_ref(q, [0, len(q)], kv, sink, case["scale"], case["window"])
+    np.testing.assert_allclose(out[:, 0, :], np.array(case["expect_o"]), rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse[:, 0], [_lse_value(s) for s in case["expect_lse"]], rtol=1e-15)
+
+
+@pytest.mark.parametrize("case", _golden()["split_cases"], ids=lambda c: c["name"])
+def test_golden_split(case):
+    n, d, ps = case["kv_len"], 4, 16
+    j = np.arange(n)
+    k = np.stack([j, -j, np.ones(n), np.zeros(n)], axis=1).astype(np.float64)
+    v = np.zeros((n, d))
+    v[j < 16, 0] = 1.0
+    v[j >= 16, 1] = 1.0
+    n_pages = n // ps
+    pool_k = np.full((n_pages, 1, ps, d), np.nan)
+    pool_v = np.full((n_pages, 1, ps, d), np.nan)
+    pages = np.arange(n_pages)[::-1].copy()          # a non-identity page table
+    for jj in range(n):
+        pool_k[pages[jj // ps], 0, jj % ps] = k[jj]
+        pool_v[pages[jj // ps], 0, jj % ps] = v[jj]
+    kv = oracle.KVCache(k=pool_k, v=pool_v, kv_indptr=np.array([0, n_pages]), paged=True,
+                        page_indices=pages, kv_len=np.array([n]), page_size=ps)
+    q = np.zeros((1, 1, d))
+    sink = np.array([_sink_value(case["sink"])])
+    o_part, lse_part = oracle.split_partials_ref(q, kv, sink, case["scale"], case["num_splits"])
+    np.testing.assert_allclose(o_part[0, 0], case["expect_o_part"], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse_part[0, 0], [_lse_value(s) for s in case["expect_lse_part"]], rtol=1e-15)
+    out, lse = oracle.merge_ref(o_part, lse_part)
+    np.testing.assert_allclose(out[0], case["expect_o"], rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(lse[0], [_lse_value(s) for s in case["expect_lse"]], rtol=1e-15)
+    out_u, lse_u = oracle.sink_attention_ref(q, [0, 1], kv, sink, case["scale"])
+    np.testing.assert_allclose(out_u[0], case["expect_o"], rtol=1e-15, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------
+# brute force
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(40))
+def test_brute_force_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), sink_kind="mixed" if seed % 5 == 0 else "normal")
+    out, lse = _oracle(p)
+    bo, bl = _brute(p)
+    np.testing.assert_allclose(out, np.array(bo), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=1e-13, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_mpmath_bounds_oracle_error(seed):
+    rng = np.random.default_rng(2000 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), max_len=6)
+    out, lse = _oracle(p)
+    mo, ml = _brute(p, fn=_loops.mp_attention)
+    assert np.max(np.abs(out - np.array(mo))) <= 1e-14
+    assert np.max(np.abs(lse - np.array(ml))) <= 1e-14
+
+
+# ----------------------------------------------------------------------------
+# library special cases and closed forms
+# ----------------------------------------------------------------------------
+
+def _torch_reference(p):
+    """Plain attention (no sink) from torch's fp64 CPU SDPA with an explicit
+    bottom-right causal/window mask, and its log-sum-exp from scipy."""
+    torch = pytest.importorskip("torch")
+    from scipy.special import logsumexp
+
+    kv = p["kv"]
+    hq = p["q"].shape[1]
+    group = hq // p["hkv"]
+    outs, lses = [], []
+    qo = p["qo_indptr"]
+    for b in range(len(qo) - 1):
+        n_q = qo[b + 1] - qo[b]
+        kk, vv = zip(*[kv.rows(b, g) for g in range(p["hkv"])])
+        kk = np.stack(kk, axis=0).repeat(group, axis=0)     # [Hq, n_k, D]
+        vv = np.stack(vv, axis=0).repeat(group, axis=0)
+        n_k = kk.shape[1]
+        qq = p["q"][qo[b]:qo[b + 1]].transpose(1, 0, 2)     # [Hq, n_q, D]
+        t = np.arange(n_q)[:, None]
+        j = np.arange(n_k)[None, :]
+        pos = n_k - n_q + t
+        mask = j <= pos
+        if p["window"] > 0:
+            mask &= j >= pos - p["window"] + 1
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(qq), torch.from_numpy(np.ascontiguousarray(kk)),
+            torch.from_numpy(np.ascontiguousarray(vv)), attn_mask=torch.from_numpy(mask),
+            scale=p["scale"]).numpy()
+        logits = p["scale"] * np.matmul(qq, kk.transpose(0, 2, 1))
+        logits = np.where(mask[None], logits, -np.inf)
+        outs.append(o.transpose(1, 0, 2))
+        lses.append(logsumexp(logits, axis=-1).T)
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_reduces_to_library_attention_when_sink_is_minus_inf(seed):
+    rng = np.random.default_rng(3000 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), max_len=40, sink_kind="-inf")
+    ro, rl = _torch_reference(p)
+    out, lse = _oracle(p)
+    np.testing.assert_allclose(out, ro, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=1e-12, atol=1e-12)
+    # sinks=None is the same as every sink at -inf
+    out2, lse2 = oracle.sink_attention_ref(p["q"], p["qo_indptr"], p["kv"], None, p["scale"], p["window"])
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_closed_form_in_the_sink(seed):
+    """Z_sigma = Z + e^sigma, so o_sigma = o_plain * sigmoid(lse_plain - sigma)
+    and lse_sigma = logaddexp(lse_plain, sigma), with the plain results taken
+    from the library."""
+    rng = np.random.default_rng(4000 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), max_len=40, sink_kind="normal")
+    p["sinks"] = rng.choice([-5.0, 0.0, 1.5, 3.0, 20.0], size=p["sinks"].shape)
+    ro, rl = _torch_reference(p)
+    out, lse = _oracle(p)
+    sig = p["sinks"][None, :]
+    factor = 1.0 / (1.0 + np.exp(sig - rl))
+    np.testing.assert_allclose(out, ro * factor[..., None], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(lse, np.logaddexp(rl, sig), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# invariants and limits
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(8))
+def test_mass_conservation(seed):
+    """Sum over visible keys of exp(s_j - lse) plus exp(sink - lse) is 1 for
+    every row: lse carries the sink's mass exactly once."""
+    rng = np.random.default_rng(5000 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), max_len=30)
+    out, lse = _oracle(p)
+    kv, qo = p["kv"], p["qo_indptr"]
+    hq = p["q"].shape[1]
+    group = hq // p["hkv"]
+    for b in range(len(qo) - 1):
+        n_q = qo[b + 1] - qo[b]
+        for t in range(n_q):
+            row = qo[b] + t
+            for h in range(hq):
+                kk, vv = kv.rows(b, h // group)
+                lo, pos = oracle.visible_range(n_q, kk.shape[0], t, p["window"])
+                s = p["scale"] * (kk[lo:pos + 1] @ p["q"][row, h])
+                mass = np.exp(s - lse[row, h]).sum() + math.exp(p["sinks"][h] - lse[row, h])
+                assert abs(mass - 1.0) <= 1e-14
+                w, w_sink = oracle.attention_weights_ref(p["q"][row, h], kk[lo:pos + 1], p["sinks"][h], p["scale"])
+                assert abs(w.sum() + w_sink - 1.0) <= 1e-14
+                np.testing.assert_allclose(w @ vv[lo:pos + 1], out[row, h], rtol=1e-13, atol=1e-14)
+
+
+def test_sink_to_plus_infinity():
+    rng = np.random.default_rng(6000)
+    p = _tiny_problem(rng, paged=True, batch=2, hq=2, hkv=1, d=4, max_len=20, sink_kind="-inf")
+    _, lse_plain = _oracle(p)
+    vmax = np.max(np.linalg.norm(p["kv"].v.reshape(-1, p["kv"].v.shape[-1]), axis=-1))
+    prev = None
+    for sig in [-2.0, 0.0, 5.0, 10.0, 20.0, 40.0, 80.0]:
+        p["sinks"] = np.full(2, sig)
+        out, lse = _oracle(p)
+        norm = np.linalg.norm(out, axis=-1)
+        assert np.all(norm <= np.exp(lse_plain - sig) * vmax * (1 + 1e-12))
+        # the output shrinks strictly as the sink grows (o_plain != 0 here)
+        if prev is not None:
+            assert np.all(norm < prev)
+        prev = norm
+    p["sinks"] = np.full(2, np.inf)
+    out, lse = _oracle(p)
+    assert np.all(out == 0.0) and np.all(np.isposinf(lse))
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_split_equals_unsplit_with_negative_control(seed):
+    rng = np.random.default_rng(7000 + seed)
+    p = _tiny_problem(rng, paged=True, max_len=70, page_size=4, qo_mode="decode")
+    full_o, full_l = _oracle(p)
+    q = p["q"]          # one row per request
+    for s in range(1, 17):
+        o_part, lse_part = oracle.split_partials_ref(q, p["kv"], p["sinks"], p["scale"], s, p["window"])
+        out, lse = oracle.merge_ref(o_part, lse_part)
+        np.testing.assert_allclose(out, full_o, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse, full_l, rtol=1e-13, atol=1e-13)
+        if s > 1:
+            # negative control: seeding every chunk adds (S - 1) extra sink masses
+            o_bad, l_bad = oracle.split_partials_ref(q, p["kv"], p["sinks"], p["scale"], s, p["window"],
+                                                     sink_in_every_chunk=True)
+            ob, lb = oracle.merge_ref(o_bad, l_bad)
+            expect = np.log(np.exp(full_l) + (s - 1) * np.exp(p["sinks"])[None, :])
+            np.testing.assert_allclose(lb, expect, rtol=1e-12)
+            assert np.max(np.abs(lb - full_l)) > 1e-3
+
+
+def test_gqa_equals_repeated_kv_mha():
+    rng = np.random.default_rng(8000)
+    p = _tiny_problem(rng, paged=False, batch=2, hq=6, hkv=2, d=4, max_len=12)
+    out, lse = _oracle(p)
+    kv = p["kv"]
+    mha = oracle.KVCache(k=np.repeat(kv.k, 3, axis=1), v=np.repeat(kv.v, 3, axis=1), kv_indptr=kv.kv_indptr)
+    out2, lse2 = oracle.sink_attention_ref(p["q"], p["qo_indptr"], mha, p["sinks"], p["scale"], p["window"])
+    np.testing.assert_array_equal(out, out2)
+    np.testing.assert_array_equal(lse, lse2)
+
+
+def test_paging_is_invisible():
+    """Two physical permutations and the contiguous layout of the same logical
+    keys give identical oracle results."""
+    rng = np.random.default_rng(9000)
+    p = _tiny_problem(rng, paged=True, batch=2, hq=4, hkv=2, d=4, max_len=37, page_size=4)
+    kv = p["kv"]
+    out1, lse1 = _oracle(p)
+    perm = rng.permutation(kv.k.shape[0])
+    k2 = np.full_like(kv.k, np.nan)
+    v2 = np.full_like(kv.v, np.nan)
+    k2[perm], v2[perm] = kv.k, kv.v
+    kv2 = oracle.KVCache(k=k2, v=v2, kv_indptr=kv.kv_indptr, paged=True, page_indices=perm[kv.page_indices],
+                         kv_len=kv.kv_len, page_size=4)
+    out2, lse2 = oracle.sink_attention_ref(p["q"], p["qo_indptr"], kv2, p["sinks"], p["scale"], p["window"])
+    np.testing.assert_array_equal(out1, out2)
+    np.testing.assert_array_equal(lse1, lse2)
+    rows = [kv.rows(b, g) for b in range(2) for g in range(2)]
+    kc = np.concatenate([np.stack([kv.rows(b, g)[0] for g in range(2)], axis=1) for b in range(2)])
+    vc = np.concatenate([np.stack([kv.rows(b, g)[1] for g in range(2)], axis=1) for b in range(2)])
+    ind = np.concatenate([[0], np.cumsum(kv.kv_len)])
+    kv3 = oracle.KVCache(k=kc, v=vc, kv_indptr=ind)
+    out3, lse3 = oracle.sink_attention_ref(p["q"], p["qo_indptr"], kv3, p["sinks"], p["scale"], p["window"])
+    np.testing.assert_array_equal(out1, out3)
+    assert rows  # noqa
+
+
+def test_window_special_cases():
+    rng = np.random.default_rng(9500)
+    p = _tiny_problem(rng, paged=False, batch=2, hq=2, hkv=1, d=3, max_len=15)
+    p["window"] = 0
+    out0, lse0 = _oracle(p)
+    p["window"] = 16          # >= every kv_len: same as no window
+    out1, lse1 = _oracle(p)
+    np.testing.assert_array_equal(out0, out1)
+    np.testing.assert_array_equal(lse0, lse1)
+
+
+def test_split_bounds_rule():
+    """Chunks are whole pages, cover [0, L) in order without overlap, and the
+    long-context shape (131072 keys, 16 chunks) gives 16 chunks of 8192."""
+    rng = np.random.default_rng(9900)
+    lens = np.concatenate([np.arange(0, 300), rng.integers(1, 200000, size=2000)])
+    for s in [1, 2, 3, 5, 7, 16, 64, 256]:
+        bnd = oracle.split_bounds_ref(lens, s)
+        assert bnd.shape == (len(lens), s, 2)
+        assert np.all(bnd[:, 0, 0] == 0)
+        assert np.all(bnd[:, -1, 1] == lens)
+        assert np.all(bnd[:, 1:, 0] == bnd[:, :-1, 1])
+        assert np.all(bnd[..., 1] >= bnd[..., 0])
+        inner = bnd[..., 0][bnd[..., 0] < lens[:, None]]
+        assert np.all(inner % 16 == 0)
+        # no chunk holds more than ceil(pages / S) pages
+        pages = -(-lens // 16)
+        assert np.all((bnd[..., 1] - bnd[..., 0]) <= (-(-pages // s) * 16)[:, None])
+    b = oracle.split_bounds_ref([131072], 16)
+    assert np.all(b[0, :, 1] - b[0, :, 0] == 8192)
+
+
+def test_merge_edge_cases():
+    o = np.array([[[1.0, 2.0], [3.0, 4.0]]])
+    assert np.all(oracle.merge_ref(o, np.array([[-np.inf, -np.inf]]))[0] == 0)
+    out, lse = oracle.merge_ref(o, np.array([[0.0, -np.inf]]))
+    np.testing.assert_array_equal(out[0], [1.0, 2.0])
+    assert lse[0] == 0.0
+    out, lse = oracle.merge_ref(o, np.array([[math.log(3.0), math.log(1.0)]]))
+    np.testing.assert_allclose(out[0], [1.5, 2.5], rtol=1e-15)
+    np.testing.assert_allclose(lse[0], math.log(4.0), rtol=1e-15)
+
+
+def test_bf16_widening_is_exact():
+    bits = np.array([0x3F80, 0xBF80, 0x4000, 0x3F00, 0x7F80, 0xFF80, 0x0001, 0x4049], dtype=np.uint16)
+    expect = [1.0, -1.0, 2.0, 0.5, np.inf, -np.inf, 2.0 ** -133, 3.140625]
+    np.testing.assert_array_equal(oracle.widen_bf16(bits), expect)
+
+
+# ----------------------------------------------------------------------------
+# planted mistakes: each must be caught by a pin above
+# ----------------------------------------------------------------------------
+
+def _brute_agrees(seed_count=12):
+    for seed in range(seed_count):
+        rng = np.random.default_rng(1000 + seed)
+        p = _tiny_problem(rng, paged=bool(seed % 2))
+        out, lse = _oracle(p)
+        bo, bl = _brute(p)
+        if not (np.allclose(out, bo, rtol=1e-13, atol=1e-13) and np.allclose(lse, bl, rtol=1e-13, atol=1e-13)):
+            return False
+    return True
+
+
+def test_planted_window_off_by_one_is_caught(monkeypatch):
+    good = sa.visible_range
+
+    def bad(n_q, n_k, t, window):
+        lo, p = good(n_q, n_k, t, window)
+        return (np.maximum(0, lo - 1) if window > 0 else lo), p
+
+    monkeypatch.setattr(sa, "visible_range", bad)
+    assert not _brute_agrees()
+
+
+def test_planted_top_left_causal_is_caught(monkeypatch):
+    good = sa.visible_range
+
+    def bad(n_q, n_k, t, window):
+        return good(n_q, n_q, t, window)
+
+    monkeypatch.setattr(sa, "visible_range", bad)
+    assert not _brute_agrees()
+
+
+def test_planted_scaled_sink_is_caught(monkeypatch):
+    good = sa._softmax_with_sink
+
+    def bad(s, vis, sink, vals):
+        return good(s, vis, sink * 0.125, vals)
+
+    monkeypatch.setattr(sa, "_softmax_with_sink", bad)
+    assert not _brute_agrees()
+
+
+def test_planted_sink_with_value_row_is_caught(monkeypatch):
+    """A sink that also contributed a value row (here: the mean of V) must fail."""
+    good = sa._softmax_with_sink
+
+    def bad(s, vis, sink, vals):
+        o, lse = good(s, vis, sink, vals)
+        if vals.shape[0]:
+            o = o + np.exp(sink - lse)[:, None] * vals.mean(axis=0)[None, :]
+        return o, lse
+
+    monkeypatch.setattr(sa, "_softmax_with_sink", bad)
+    assert not _brute_agrees()
+
+
+def test_planted_wrong_gather_is_caught(monkeypatch):
+    good = sa.KVCache.rows
+
+    def bad(self, b, g, lo=0, hi=None):
+        kk, vv = good(self, b, g, lo, hi)
+        return kk, vv[::-1].copy()
+
+    monkeypatch.setattr(sa.KVCache, "rows", bad)
+    assert not _brute_agrees()

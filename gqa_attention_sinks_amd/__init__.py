@@ -1,4 +1,22 @@
 """Grouped-query flash attention with per-head learned sinks for MI355X (gfx950).
 
-``workloads`` holds the seeded input generators.
+The compute lives in ``libsinkattn.so`` (hand-written HIP kernels behind a
+C ABI declared in ``include/sinkattn.h``).  This package is the thin Python
+binding (``binding``) plus the seeded input generators (``workloads``).
+Importing it does not load the library; the first call does, and raises
+``SinkAttnError`` if the library has not been built.
 """
+
+from .binding import (  # noqa: F401
+    EXPORTED,
+    SinkAttnError,
+    abi_version,
+    decode_paged,
+    kv_descriptor,
+    library_path,
+    load_library,
+    merge,
+    pick_num_splits,
+    prefill,
+    split_bounds,
+)

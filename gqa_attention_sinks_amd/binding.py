@@ -1,0 +1,289 @@
+"""Thin ctypes binding of libsinkattn (include/sinkattn.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, their ``data_ptr()`` and torch's current HIP stream are passed to
+the C entry points, and a non-OK status raises ``SinkAttnError``.  All
+attention arithmetic runs in the library's HIP kernels; there is no fallback
+path.  torch supplies device memory and streams.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+HEAD_DIM = 64
+PAGE_SIZE = 16
+MAX_SPLITS = 256
+EXPORTED = (
+    "sinkattn_prefill",
+    "sinkattn_decode_paged",
+    "sinkattn_merge",
+    "sinkattn_split_bounds",
+    "sinkattn_pick_num_splits",
+    "sinkattn_status_string",
+    "sinkattn_last_error",
+    "sinkattn_abi_version",
+)
+
+
+class SinkAttnError(RuntimeError):
+    """A libsinkattn call returned a non-OK status (or the library is missing)."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"libsinkattn status {status}: {message}")
+        self.status = status
+
+
+class _KV(ctypes.Structure):
+    _fields_ = [
+        ("k", ctypes.c_void_p),
+        ("v", ctypes.c_void_p),
+        ("paged", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("kv_indptr", ctypes.c_void_p),
+        ("page_indices", ctypes.c_void_p),
+        ("kv_len", ctypes.c_void_p),
+    ]
+
+
+def library_path() -> str:
+    return os.environ.get("SINKATTN_LIB", os.path.join(_HERE, "libsinkattn.so"))
+
+
+def load_library():
+    """Load libsinkattn.so once; raise if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise SinkAttnError(-1, f"{path} is missing: build it with "
+                                "`python -m gqa_attention_sinks_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+    lib.sinkattn_prefill.argtypes = [vp, vp, ctypes.POINTER(_KV), vp, vp, vp, i32, i32, i32, i32, i32,
+                                     f32, i32, vp]
+    lib.sinkattn_prefill.restype = i32
+    lib.sinkattn_decode_paged.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp, i32, i32,
+                                          i32, i32, f32, i32, vp]
+    lib.sinkattn_decode_paged.restype = i32
+    lib.sinkattn_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    lib.sinkattn_merge.restype = i32
+    lib.sinkattn_split_bounds.argtypes = [vp, i32, i32, i32, vp]
+    lib.sinkattn_split_bounds.restype = i32
+    lib.sinkattn_pick_num_splits.argtypes = [vp, i32, i32]
+    lib.sinkattn_pick_num_splits.restype = i32
+    lib.sinkattn_status_string.argtypes = [i32]
+    lib.sinkattn_status_string.restype = ctypes.c_char_p
+    lib.sinkattn_last_error.argtypes = []
+    lib.sinkattn_last_error.restype = ctypes.c_char_p
+    lib.sinkattn_abi_version.argtypes = []
+    lib.sinkattn_abi_version.restype = i32
+    _LIB = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise SinkAttnError(status, lib.sinkattn_last_error().decode())
+
+
+def abi_version() -> int:
+    return load_library().sinkattn_abi_version()
+
+
+# --------------------------------------------------------------------------
+# tensor checks
+# --------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev(t, name, dtype, shape=None):
+    torch = _torch()
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
+    torch = _torch()
+    paged = page_indices is not None
+    _dev(k, "k", torch.bfloat16)
+    _dev(v, "v", torch.bfloat16)
+    if k.shape != v.shape:
+        raise ValueError("k and v must have the same shape")
+    _dev(kv_indptr, "kv_indptr", torch.int32)
+    if paged:
+        if k.dim() != 4 or k.shape[2] != PAGE_SIZE or k.shape[3] != HEAD_DIM:
+            raise ValueError("paged k/v must be [num_pages, Hkv, 16, 64]")
+        _dev(page_indices, "page_indices", torch.int32)
+        _dev(kv_len, "kv_len", torch.int32)
+    elif k.dim() != 3 or k.shape[2] != HEAD_DIM:
+        raise ValueError("contiguous k/v must be [total_kv, Hkv, 64]")
+    return _KV(k.data_ptr(), v.data_ptr(), int(paged), PAGE_SIZE, kv_indptr.data_ptr(),
+               page_indices.data_ptr() if paged else None, kv_len.data_ptr() if paged else None)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int = 0,
+            page_indices=None, kv_len=None, out=None, lse=None, return_lse: bool = False,
+            stream=None):
+    """Causal / sliding-window prefill (``sinkattn_prefill``).
+
+    ``q`` [total_q, Hq, 64] bf16; ``qo_indptr`` [B+1] int32.  Contiguous KV:
+    ``k``/``v`` [total_kv, Hkv, 64] with ``kv_indptr`` row offsets.  Paged KV:
+    ``k``/``v`` [num_pages, Hkv, 16, 64] with ``kv_indptr`` page offsets,
+    ``page_indices`` and ``kv_len``.  ``sinks`` [Hq] fp32 or None.
+    Returns ``out`` (and ``lse`` [total_q, Hq] fp32 when asked).
+    """
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [total_q, Hq, 64]")
+    total_q, hq, _ = q.shape
+    _dev(qo_indptr, "qo_indptr", torch.int32)
+    batch = qo_indptr.numel() - 1
+    kvs = _kv_struct(k, v, kv_indptr, page_indices, kv_len)
+    hkv = k.shape[1]
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32, (hq,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, q.shape)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (total_q, hq))
+    lib = load_library()
+    _check(lib.sinkattn_prefill(_ptr(q), _ptr(qo_indptr), ctypes.byref(kvs), _ptr(sinks), _ptr(out),
+                                _ptr(lse), batch, total_q, hq, hkv, HEAD_DIM, float(sm_scale),
+                                int(window), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm_scale: float,
+                 num_splits: int = 1, window: int = 0, out=None, o_part=None, lse_part=None,
+                 lse=None, return_lse: bool = False, merge: bool = True, stream=None):
+    """One query token per request over a paged cache (``sinkattn_decode_paged``).
+
+    With ``num_splits`` > 1 the per-chunk partials ``o_part`` [B, Hq, S, 64]
+    and ``lse_part`` [B, Hq, S] (allocated if not given) are written; with
+    ``merge`` they are also merged into ``out`` in the same call.  Returns
+    ``out`` (and ``lse``), or ``(o_part, lse_part)`` when ``merge`` is False.
+    """
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, Hq, 64]")
+    batch, hq, _ = q.shape
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    hkv = k_pool.shape[1]
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32, (hq,))
+    s = int(num_splits)
+    if s > 1:
+        if o_part is None:
+            o_part = torch.empty((batch, hq, s, HEAD_DIM), dtype=torch.float32, device=q.device)
+        if lse_part is None:
+            lse_part = torch.empty((batch, hq, s), dtype=torch.float32, device=q.device)
+        _dev(o_part, "o_part", torch.float32, (batch, hq, s, HEAD_DIM))
+        _dev(lse_part, "lse_part", torch.float32, (batch, hq, s))
+    else:
+        o_part = lse_part = None
+    want_out = s == 1 or merge
+    if want_out and out is None:
+        out = torch.empty_like(q)
+    if out is not None:
+        _dev(out, "out", torch.bfloat16, q.shape)
+    if want_out and return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, hq))
+    lib = load_library()
+    _check(lib.sinkattn_decode_paged(_ptr(q), ctypes.byref(kvs), _ptr(sinks), s,
+                                     _ptr(out if want_out else None), _ptr(o_part), _ptr(lse_part),
+                                     _ptr(lse if want_out else None), batch, hq, hkv, HEAD_DIM,
+                                     float(sm_scale), int(window), _stream(stream)))
+    if not want_out:
+        return o_part, lse_part
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def merge(o_part, lse_part, out=None, lse=None, return_lse: bool = False, stream=None):
+    """LSE merge of split partials (``sinkattn_merge``): ``o_part`` [R, H, S, 64]
+    fp32 and ``lse_part`` [R, H, S] fp32 -> ``out`` [R, H, 64] bf16."""
+    torch = _torch()
+    _dev(o_part, "o_part", torch.float32)
+    if o_part.dim() != 4 or o_part.shape[3] != HEAD_DIM:
+        raise ValueError("o_part must be [rows, heads, splits, 64]")
+    rows, heads, s, _ = o_part.shape
+    _dev(lse_part, "lse_part", torch.float32, (rows, heads, s))
+    if out is None:
+        out = torch.empty((rows, heads, HEAD_DIM), dtype=torch.bfloat16, device=o_part.device)
+    _dev(out, "out", torch.bfloat16, (rows, heads, HEAD_DIM))
+    if return_lse and lse is None:
+        lse = torch.empty((rows, heads), dtype=torch.float32, device=o_part.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (rows, heads))
+    lib = load_library()
+    _check(lib.sinkattn_merge(_ptr(o_part), _ptr(lse_part), rows, heads, s, HEAD_DIM, _ptr(out),
+                              _ptr(lse), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def split_bounds(kv_len_host, num_splits: int, page_size: int = PAGE_SIZE) -> np.ndarray:
+    """Host-only chunk rule of the split decode: int32 [B, S, 2] token ranges."""
+    lens = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    out = np.zeros((len(lens), num_splits, 2), dtype=np.int32)
+    lib = load_library()
+    _check(lib.sinkattn_split_bounds(lens.ctypes.data_as(ctypes.c_void_p), len(lens), page_size,
+                                     num_splits, out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def pick_num_splits(kv_len_host, num_kv_heads: int) -> int:
+    """Host-only split count suggested for a decode batch."""
+    lens = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    return int(load_library().sinkattn_pick_num_splits(lens.ctypes.data_as(ctypes.c_void_p), len(lens),
+                                                       num_kv_heads))
+
+
+def raw_library():
+    """The ctypes handle, for callers that drive the C ABI directly."""
+    return load_library()
+
+
+def kv_descriptor(k, v, kv_indptr, page_indices=None, kv_len=None) -> _KV:
+    """Build the ``sinkattn_kv`` struct for direct C-ABI calls."""
+    return _kv_struct(k, v, kv_indptr, page_indices, kv_len)

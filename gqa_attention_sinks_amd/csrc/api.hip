@@ -1,0 +1,255 @@
+// C ABI of libsinkattn: argument validation on the host, then kernel launches
+// on the caller's stream.  Declarations and the contract of every entry point
+// are in include/sinkattn.h.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kernel_args.hpp"
+#include "sinkattn.h"
+
+namespace sinkattn {
+int prefill_rows_per_tile();
+}
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sinkattn_status fail(sinkattn_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+sinkattn_status fail(sinkattn_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+sinkattn_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SINKATTN_OK;
+  return fail(SINKATTN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define REQUIRE(cond, code, ...) \
+  do {                           \
+    if (!(cond)) return fail(code, __VA_ARGS__); \
+  } while (0)
+
+sinkattn_status check_heads(int32_t batch, int32_t hq, int32_t hkv, int32_t head_dim, float sm_scale,
+                            int32_t window) {
+  REQUIRE(batch >= 1, SINKATTN_ERR_INVALID_ARG, "batch must be >= 1 (got %d)", batch);
+  REQUIRE(hq >= 1 && hkv >= 1, SINKATTN_ERR_INVALID_ARG, "head counts must be >= 1 (Hq=%d, Hkv=%d)", hq, hkv);
+  REQUIRE(hq % hkv == 0, SINKATTN_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", hq, hkv);
+  REQUIRE(head_dim == SINKATTN_HEAD_DIM, SINKATTN_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
+  REQUIRE(hq / hkv <= 16, SINKATTN_ERR_UNSUPPORTED, "Hq/Hkv = %d unsupported (at most 16)", hq / hkv);
+  REQUIRE(isfinite(sm_scale) && sm_scale > 0.f, SINKATTN_ERR_INVALID_ARG, "sm_scale must be finite and > 0");
+  REQUIRE(window >= 0, SINKATTN_ERR_INVALID_ARG, "window must be >= 0 (got %d)", window);
+  return SINKATTN_OK;
+}
+
+sinkattn_status check_kv(const sinkattn_kv* kv, bool need_paged) {
+  REQUIRE(kv != nullptr, SINKATTN_ERR_INVALID_ARG, "kv descriptor is NULL");
+  REQUIRE(kv->k != nullptr && kv->v != nullptr, SINKATTN_ERR_INVALID_ARG, "kv->k and kv->v are required");
+  REQUIRE(kv->kv_indptr != nullptr, SINKATTN_ERR_INVALID_ARG, "kv->kv_indptr is required");
+  REQUIRE(kv->paged == 0 || kv->paged == 1, SINKATTN_ERR_INVALID_ARG, "kv->paged must be 0 or 1");
+  if (need_paged) REQUIRE(kv->paged == 1, SINKATTN_ERR_INVALID_ARG, "decode needs a paged KV cache");
+  if (kv->paged) {
+    REQUIRE(kv->page_indices != nullptr && kv->kv_len != nullptr, SINKATTN_ERR_INVALID_ARG,
+            "paged KV needs page_indices and kv_len");
+    REQUIRE(kv->page_size == SINKATTN_PAGE_SIZE, SINKATTN_ERR_UNSUPPORTED,
+            "page_size %d unsupported (only 16)", kv->page_size);
+  }
+  return SINKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const sinkattn_kv* kv,
+                                 const float* sinks, void* out, float* lse, int32_t batch,
+                                 int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float sm_scale, int32_t window, void* stream) {
+  REQUIRE(q != nullptr && qo_indptr != nullptr && out != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "q, qo_indptr and out are required");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_kv(kv, false)) != SINKATTN_OK) return st;
+  REQUIRE(total_q >= batch, SINKATTN_ERR_INVALID_ARG, "total_q (%d) must be >= batch (%d): every request has a query row",
+          total_q, batch);
+
+  const int bm = sinkattn::prefill_rows_per_tile();
+  sinkattn::PrefillArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.qo_indptr = qo_indptr;
+  a.k = static_cast<const uint16_t*>(kv->k);
+  a.v = static_cast<const uint16_t*>(kv->v);
+  a.kv_indptr = kv->kv_indptr;
+  a.page_indices = kv->page_indices;
+  a.kv_len = kv->kv_len;
+  a.sinks = sinks;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.scale_log2 = sm_scale * 1.4426950408889634f;
+  a.batch = batch;
+  a.num_qo_heads = num_qo_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.group = num_qo_heads / num_kv_heads;
+  a.window = window;
+  a.paged = kv->paged;
+  // single-row requests (decode rows of a mixed batch) go to the decode kernel when paged
+  a.skip_single_rows = kv->paged;
+  const long slots = (long)total_q / bm + batch;   // >= sum over requests of ceil(n_q / bm)
+  REQUIRE(slots * num_qo_heads < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  a.num_slots = (int32_t)slots;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(sinkattn::launch_prefill(a, total_q, s), "prefill launch")) != SINKATTN_OK) return st;
+  if (kv->paged) {
+    sinkattn::DecodeArgs d{};
+    d.q = a.q;
+    d.k_pool = a.k;
+    d.v_pool = a.v;
+    d.page_indptr = kv->kv_indptr;
+    d.page_indices = kv->page_indices;
+    d.kv_len = kv->kv_len;
+    d.qo_indptr = qo_indptr;
+    d.sinks = sinks;
+    d.out = a.out;
+    d.lse = lse;
+    d.scale_log2 = a.scale_log2;
+    d.batch = batch;
+    d.num_qo_heads = num_qo_heads;
+    d.num_kv_heads = num_kv_heads;
+    d.group = a.group;
+    d.num_splits = 1;
+    d.window = window;
+    if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
+  }
+  return SINKATTN_OK;
+}
+
+sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                      int32_t num_splits, void* out, float* o_part,
+                                      float* lse_part, float* lse, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float sm_scale, int32_t window,
+                                      void* stream) {
+  REQUIRE(q != nullptr, SINKATTN_ERR_INVALID_ARG, "q is required");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_kv(kv, true)) != SINKATTN_OK) return st;
+  REQUIRE(num_splits >= 1 && num_splits <= SINKATTN_MAX_SPLITS, SINKATTN_ERR_INVALID_ARG,
+          "num_splits must be in [1, %d] (got %d)", SINKATTN_MAX_SPLITS, num_splits);
+  if (num_splits == 1) {
+    REQUIRE(out != nullptr, SINKATTN_ERR_INVALID_ARG, "num_splits == 1 needs out");
+  } else {
+    REQUIRE(o_part != nullptr && lse_part != nullptr, SINKATTN_ERR_INVALID_ARG,
+            "num_splits > 1 needs o_part and lse_part");
+  }
+  sinkattn::DecodeArgs d{};
+  d.q = static_cast<const uint16_t*>(q);
+  d.k_pool = static_cast<const uint16_t*>(kv->k);
+  d.v_pool = static_cast<const uint16_t*>(kv->v);
+  d.page_indptr = kv->kv_indptr;
+  d.page_indices = kv->page_indices;
+  d.kv_len = kv->kv_len;
+  d.qo_indptr = nullptr;
+  d.sinks = sinks;
+  d.out = static_cast<uint16_t*>(out);
+  d.lse = lse;
+  d.o_part = o_part;
+  d.lse_part = lse_part;
+  d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.batch = batch;
+  d.num_qo_heads = num_qo_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.group = num_qo_heads / num_kv_heads;
+  d.num_splits = num_splits;
+  d.window = window;
+  REQUIRE((long)batch * num_kv_heads * num_splits < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
+  if (num_splits > 1 && out != nullptr) {
+    sinkattn::MergeArgs m{o_part, lse_part, static_cast<uint16_t*>(out), lse, batch, num_qo_heads, num_splits};
+    if ((st = hip_status(sinkattn::launch_merge(m, s), "merge launch")) != SINKATTN_OK) return st;
+  }
+  return SINKATTN_OK;
+}
+
+sinkattn_status sinkattn_merge(const float* o_part, const float* lse_part, int32_t rows,
+                               int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
+                               float* lse_out, void* stream) {
+  REQUIRE(o_part != nullptr && lse_part != nullptr && out != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "o_part, lse_part and out are required");
+  REQUIRE(rows >= 1 && num_heads >= 1, SINKATTN_ERR_INVALID_ARG, "rows and num_heads must be >= 1");
+  REQUIRE(num_splits >= 1 && num_splits <= SINKATTN_MAX_SPLITS, SINKATTN_ERR_INVALID_ARG,
+          "num_splits must be in [1, %d] (got %d)", SINKATTN_MAX_SPLITS, num_splits);
+  REQUIRE(head_dim == SINKATTN_HEAD_DIM, SINKATTN_ERR_UNSUPPORTED, "head_dim %d unsupported (only 64)", head_dim);
+  REQUIRE((long)rows * num_heads < (1L << 31) * 4L, SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  sinkattn::MergeArgs m{o_part, lse_part, static_cast<uint16_t*>(out), lse_out, rows, num_heads, num_splits};
+  return hip_status(sinkattn::launch_merge(m, static_cast<hipStream_t>(stream)), "merge launch");
+}
+
+sinkattn_status sinkattn_split_bounds(const int32_t* kv_len_host, int32_t batch, int32_t page_size,
+                                      int32_t num_splits, int32_t* bounds_host) {
+  REQUIRE(kv_len_host != nullptr && bounds_host != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "kv_len_host and bounds_host are required");
+  REQUIRE(batch >= 0, SINKATTN_ERR_INVALID_ARG, "batch must be >= 0");
+  REQUIRE(page_size >= 1, SINKATTN_ERR_INVALID_ARG, "page_size must be >= 1");
+  REQUIRE(num_splits >= 1 && num_splits <= SINKATTN_MAX_SPLITS, SINKATTN_ERR_INVALID_ARG,
+          "num_splits must be in [1, %d]", SINKATTN_MAX_SPLITS);
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = kv_len_host[b];
+    REQUIRE(len >= 0, SINKATTN_ERR_INVALID_ARG, "kv_len[%d] < 0", b);
+    const int64_t n_pages = (len + page_size - 1) / page_size;
+    const int64_t ppc = (n_pages + num_splits - 1) / num_splits;
+    for (int32_t c = 0; c < num_splits; ++c) {
+      const int64_t p0 = c * ppc < n_pages ? c * ppc : n_pages;
+      const int64_t p1 = (c + 1) * ppc < n_pages ? (c + 1) * ppc : n_pages;
+      const int64_t lo = p0 * page_size < len ? p0 * page_size : len;
+      const int64_t hi = p1 * page_size < len ? p1 * page_size : len;
+      bounds_host[((int64_t)b * num_splits + c) * 2 + 0] = (int32_t)lo;
+      bounds_host[((int64_t)b * num_splits + c) * 2 + 1] = (int32_t)hi;
+    }
+  }
+  return SINKATTN_OK;
+}
+
+int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int32_t num_kv_heads) {
+  if (kv_len_host == nullptr || batch < 1 || num_kv_heads < 1) return 1;
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) max_len = kv_len_host[b] > max_len ? kv_len_host[b] : max_len;
+  const int64_t max_pages = (max_len + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE;
+  // aim for about four work units per compute unit (256 CUs), but keep
+  // chunks at least 16 pages long
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  int64_t s = (1024 + units - 1) / units;
+  const int64_t cap = max_pages / 16 > 1 ? max_pages / 16 : 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  if (s > SINKATTN_MAX_SPLITS) s = SINKATTN_MAX_SPLITS;
+  return (int32_t)s;
+}
+
+const char* sinkattn_status_string(sinkattn_status status) {
+  switch (status) {
+    case SINKATTN_OK: return "ok";
+    case SINKATTN_ERR_INVALID_ARG: return "invalid argument";
+    case SINKATTN_ERR_UNSUPPORTED: return "unsupported";
+    case SINKATTN_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sinkattn_abi_version(void) { return SINKATTN_ABI_VERSION; }
+
+}  // extern "C"

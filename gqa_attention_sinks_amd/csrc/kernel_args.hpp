@@ -1,0 +1,62 @@
+// Argument blocks passed by value to the kernels, and the host-side launcher
+// declarations shared by the C-ABI layer (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sinkattn {
+
+// One query token per request over a paged cache, split into chunks of whole
+// pages; see sinkattn_decode_paged in include/sinkattn.h.
+struct DecodeArgs {
+  const uint16_t* q;          // [rows, Hq, 64] bf16
+  const uint16_t* k_pool;     // [num_pages, Hkv, 16, 64] bf16
+  const uint16_t* v_pool;
+  const int32_t* page_indptr; // [B+1]
+  const int32_t* page_indices;
+  const int32_t* kv_len;      // [B]
+  const int32_t* qo_indptr;   // optional: mixed batch; only requests with one query row are
+                              // handled and their row is qo_indptr[b]
+  const float* sinks;         // [Hq] or null
+  uint16_t* out;              // num_splits == 1: [rows, Hq, 64] bf16
+  float* lse;                 // num_splits == 1: optional [rows, Hq]
+  float* o_part;              // num_splits > 1: [B, Hq, S, 64]
+  float* lse_part;            // num_splits > 1: [B, Hq, S]
+  float scale_log2;           // sm_scale * log2(e)
+  int32_t batch, num_qo_heads, num_kv_heads, group, num_splits, window;
+};
+
+struct MergeArgs {
+  const float* o_part;        // [rows, H, S, 64]
+  const float* lse_part;      // [rows, H, S]
+  uint16_t* out;              // [rows, H, 64]
+  float* lse;                 // optional [rows, H]
+  int32_t rows, num_heads, num_splits;
+};
+
+// Causal / sliding-window prefill, one query head and a tile of query rows
+// per workgroup.
+struct PrefillArgs {
+  const uint16_t* q;          // [total_q, Hq, 64]
+  const int32_t* qo_indptr;   // [B+1]
+  const uint16_t* k;          // contiguous [total_kv, Hkv, 64] or pool [P, Hkv, 16, 64]
+  const uint16_t* v;
+  const int32_t* kv_indptr;   // contiguous: row offsets; paged: offsets into page_indices
+  const int32_t* page_indices;
+  const int32_t* kv_len;      // paged only
+  const float* sinks;
+  uint16_t* out;              // [total_q, Hq, 64]
+  float* lse;                 // optional [total_q, Hq]
+  float scale_log2;
+  int32_t batch, num_qo_heads, num_kv_heads, group, window;
+  int32_t paged;
+  int32_t skip_single_rows;   // requests with one query row are left to the decode kernel
+  int32_t num_slots;          // tile slots launched (upper bound on tiles)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream);
+
+}  // namespace sinkattn

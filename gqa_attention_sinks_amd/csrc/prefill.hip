@@ -1,0 +1,326 @@
+// Causal / sliding-window prefill with per-head attention sinks.
+//
+// Method: Perplexity blog "GPT-OSS on day 0" (French rendering "GPT-OSS au
+// jour J"), section "Kernels for GPT-OSS > Sink attention": the sink is one
+// more term of the softmax; the streaming softmax (running max m, scale d)
+// starts from (sink, 1), so the sink costs nothing per key.
+//
+// Work decomposition (gfx950):
+//   workgroup = (tile of 128 query rows of one request, one query head);
+//   4 waves x 32 query rows.  Consecutive workgroup ids walk the KV heads
+//   first, so with 8 KV heads and 8 XCDs each XCD's L2 serves one KV head.
+//   Tiles of a request are issued longest first (causal work grows with the
+//   row index).
+//   Per KV tile of 64 keys (K and V staged in LDS, double buffered, 16-byte
+//   chunks XOR-swizzled by key):
+//     S^T[64 keys x 32 rows] = K . Q^T    -> 8 x MFMA 32x32x16 bf16 (Q^T in registers)
+//     base-2 online softmax on the accumulator: each lane holds one query row
+//     and 32 of its keys, so the row max needs one exchange with lane ^ 32
+//     O^T[64 dims x 32 rows] += V^T . P^T -> 8 x MFMA 32x32x16 bf16
+//       (P^T is the converted score accumulator; V^T comes from the natural
+//        [key][dim] LDS tile through ds_read_b64_tr_b16)
+//   Masking is applied only on tiles that cross the causal diagonal or the
+//   window's lower edge.
+
+#include "device_common.hpp"
+#include "kernel_args.hpp"
+
+namespace sinkattn {
+namespace {
+
+constexpr int kBM = 128;   // query rows per workgroup
+constexpr int kBN = 64;    // keys per tile
+constexpr int kWaves = 4;
+constexpr int kTileBytes = kBN * kHeadDim * 2;   // 8 KiB
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+__device__ __forceinline__ int tile_swizzle(int key, int chunk) {
+  return key * 128 + ((chunk ^ (key & 7)) << 4);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(uint8_t* p) {
+  return (__attribute__((address_space(3))) T*)(p);
+}
+
+// Find the (request, tile) handled by tile slot `slot`: tiles are numbered
+// request by request; every thread sums a run of requests, then a block scan.
+__device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* out_b, int* out_tile) {
+  const int tid = threadIdx.x;
+  const int per = (a.batch + kWaves * 64 - 1) / (kWaves * 64);
+  const int b0 = min(tid * per, a.batch);
+  const int b1 = min(b0 + per, a.batch);
+  int local = 0;
+  for (int b = b0; b < b1; ++b) {
+    const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    if (!(a.skip_single_rows && n == 1)) local += (n + kBM - 1) / kBM;
+  }
+  s_scan[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < kWaves * 64; off <<= 1) {
+    const int v = tid >= off ? s_scan[tid - off] : 0;
+    __syncthreads();
+    s_scan[tid] += v;
+    __syncthreads();
+  }
+  const int excl = s_scan[tid] - local;
+  __shared__ int s_found[2];
+  if (tid == 0) s_found[0] = -1;
+  __syncthreads();
+  if (slot >= excl && slot < excl + local) {
+    int base = excl;
+    for (int b = b0; b < b1; ++b) {
+      const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
+      const int nt = (a.skip_single_rows && n == 1) ? 0 : (n + kBM - 1) / kBM;
+      if (slot < base + nt) {
+        s_found[0] = b;
+        s_found[1] = nt - 1 - (slot - base);   // longest tile first
+        break;
+      }
+      base += nt;
+    }
+  }
+  __syncthreads();
+  *out_b = s_found[0];
+  *out_tile = s_found[1];
+  return s_found[0] >= 0;
+}
+
+template <bool PAGED>
+__global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
+  __shared__ int s_scan[kWaves * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int row32 = lane & 31;   // query row within the wave (MFMA column)
+  const int half = lane >> 5;
+
+  int id = blockIdx.x;
+  const int g = id % a.num_kv_heads;
+  id /= a.num_kv_heads;
+  const int hg = id % a.group;
+  const int slot = id / a.group;
+  const int head = g * a.group + hg;
+
+  int b, tile;
+  if (!locate_tile(a, slot, s_scan, &b, &tile)) return;
+
+  const int q_begin = a.qo_indptr[b];
+  const int n_q = a.qo_indptr[b + 1] - q_begin;
+  int n_k, kv_begin = 0;
+  if (PAGED) {
+    n_k = a.kv_len[b];
+  } else {
+    kv_begin = a.kv_indptr[b];
+    n_k = a.kv_indptr[b + 1] - kv_begin;
+  }
+  const int shift = n_k - n_q;   // row t sits at key position shift + t
+  const int t0 = tile * kBM;
+  const int t_last = min(t0 + kBM, n_q) - 1;
+  const int W = a.window;
+  const int lo_first = W > 0 ? max(0, shift + t0 - W + 1) : 0;
+  const int k_first = (lo_first / kBN) * kBN;
+  const int k_end = shift + t_last + 1;   // exclusive
+  const int ntiles = (k_end - k_first + kBN - 1) / kBN;
+
+  // this wave's rows and the row this lane owns
+  const int wt0 = t0 + 32 * wave;
+  const int my_t = wt0 + row32;
+  const int my_p = shift + my_t;
+  const int my_lo = W > 0 ? my_p - W + 1 : 0;
+  const int wp_min = shift + wt0;
+  const int wp_max = shift + min(wt0 + 31, t_last);
+  const bool wave_live = wt0 <= t_last;
+
+  // Q^T operand: column = row, k = dims 16*ks + 8*half + e
+  bf16x8 qop[4];
+  {
+    const bool ok = my_t < n_q;
+    const uint16_t* qp = a.q + ((size_t)(q_begin + (ok ? my_t : 0)) * a.num_qo_heads + head) * kHeadDim + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      qop[ks] = ok ? __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks)) : bf16x8{};
+  }
+
+  float m = kNegInf, dsum = 0.f;
+  if (a.sinks != nullptr) {
+    m = a.sinks[head] * kLog2e;
+    dsum = half == 0 ? 1.f : 0.f;
+  }
+  f32x16 acc[2] = {};
+
+  // tile loader: thread -> (key = tid / 4, 32 bytes at dims 16 * (tid % 4))
+  const int ld_key = tid >> 2;
+  const int ld_c = (tid & 3) * 2;   // first 16-byte chunk
+  const size_t g_off = (size_t)g * (PAGED ? kPageSize * kHeadDim : kHeadDim);
+  auto load_tile = [&](int kt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
+    const int key = kt + ld_key;
+    if (key < n_k) {
+      size_t row;
+      if (PAGED) {
+        const int page = a.page_indices[a.kv_indptr[b] + key / kPageSize];
+        row = ((size_t)page * a.num_kv_heads * kPageSize + key % kPageSize) * kHeadDim + g_off;
+      } else {
+        row = (size_t)(kv_begin + key) * a.num_kv_heads * kHeadDim + g_off;
+      }
+      const uint16_t* kp = a.k + row + ld_c * 8;
+      const uint16_t* vp = a.v + row + ld_c * 8;
+      kr[0] = ldg16(kp);
+      kr[1] = ldg16(kp + 8);
+      vr[0] = ldg16(vp);
+      vr[1] = ldg16(vp + 8);
+    } else {
+      kr[0] = kr[1] = vr[0] = vr[1] = u32x4{};
+    }
+  };
+  auto store_tile = [&](int stage, const u32x4 (&kr)[2], const u32x4 (&vr)[2]) {
+    uint8_t* ks = smem + stage * 2 * kTileBytes;
+    uint8_t* vs = ks + kTileBytes;
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c)) = kr[0];
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c + 1)) = kr[1];
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c)) = vr[0];
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c + 1)) = vr[1];
+  };
+
+  {
+    u32x4 kr[2], vr[2];
+    load_tile(k_first, kr, vr);
+    store_tile(0, kr, vr);
+  }
+  __syncthreads();
+
+  const int gr = lane >> 4;    // 16-lane group
+  const int j16 = lane & 15;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt = k_first + it * kBN;
+    u32x4 kr[2], vr[2];
+    const bool more = it + 1 < ntiles;
+    if (more) load_tile(kt + kBN, kr, vr);
+
+    const bool wave_skip = !wave_live || kt > wp_max || (W > 0 && kt + kBN - 1 < wp_min - W + 1);
+    if (!wave_skip) {
+      uint8_t* ks = smem + (it & 1) * 2 * kTileBytes;
+      uint8_t* vs = ks + kTileBytes;
+      // S^T = K . Q^T
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const int key = 32 * kb + row32;
+#pragma unroll
+        for (int kstep = 0; kstep < 4; ++kstep) {
+          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + tile_swizzle(key, 2 * kstep + half));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[kstep], s[kb], 0, 0, 0);
+        }
+      }
+      const bool need_mask = (kt + kBN - 1 > wp_min) || (W > 0 && kt < wp_max - W + 1);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = kt + 32 * kb + 8 * (i >> 2) + 4 * half + (i & 3);
+            const bool vis = j <= my_p && j >= my_lo;
+            s[kb][i] = vis ? s[kb][i] : kNegInf;
+          }
+      }
+      float mx = kNegInf;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+      const float m_new = fmaxf(m, mx * a.scale_log2);
+      const float alpha = (m == m_new) ? 1.f : exp2_hw(m - m_new);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      m = m_new;
+      dsum *= alpha;
+#pragma unroll
+      for (int db = 0; db < 2; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
+
+      // P^T operands: MFMA r covers keys 16r .. 16r+15 of the tile
+      bf16x8 pop[4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = exp2_hw(__builtin_fmaf(s[kb][8 * hh + e], a.scale_log2, -m_use));
+          u32x4 pk;
+          pk[0] = pack_bf16x2(p[0], p[1]);
+          pk[1] = pack_bf16x2(p[2], p[3]);
+          pk[2] = pack_bf16x2(p[4], p[5]);
+          pk[3] = pack_bf16x2(p[6], p[7]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dsum = add_bf16x2(pk[e], dsum);
+          pop[2 * kb + hh] = __builtin_bit_cast(bf16x8, pk);
+        }
+
+      // O^T += V^T . P^T ; V^T rows from transposed LDS reads
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key_a = 16 * r + 4 * half + (j16 >> 2);
+        const int key_b = key_a + 8;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int chunk = 4 * db + 2 * (gr & 1) + ((j16 & 3) >> 1);
+          const int sub = 8 * (j16 & 1);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_a, chunk) + sub));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_b, chunk) + sub));
+          typedef __attribute__((ext_vector_type(8))) short i16x8;
+          const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pop[r], acc[db], 0, 0, 0);
+        }
+      }
+    }
+
+    if (more) store_tile((it + 1) & 1, kr, vr);
+    __syncthreads();
+  }
+
+  if (!wave_live) return;
+  dsum += shfl_xor_f32(dsum, 32);
+  if (my_t >= n_q) return;
+  const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
+  const size_t orow = ((size_t)(q_begin + my_t) * a.num_qo_heads + head) * kHeadDim;
+#pragma unroll
+  for (int db = 0; db < 2; ++db)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d0 = 32 * db + 8 * q4 + 4 * half;
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[db][4 * q4 + 0] * inv, acc[db][4 * q4 + 1] * inv);
+      w[1] = pack_bf16x2(acc[db][4 * q4 + 2] * inv, acc[db][4 * q4 + 3] * inv);
+      *reinterpret_cast<u32x2*>(a.out + orow + d0) = w;
+    }
+  if (a.lse != nullptr && half == 0)
+    a.lse[(size_t)(q_begin + my_t) * a.num_qo_heads + head] = (m + log2_hw(dsum)) * kLn2;
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream) {
+  (void)total_q;
+  const long blocks = (long)a.num_slots * a.num_qo_heads;
+  if (blocks <= 0) return hipSuccess;
+  if (a.paged)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+int prefill_rows_per_tile() { return kBM; }
+
+}  // namespace sinkattn

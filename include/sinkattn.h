@@ -1,0 +1,170 @@
+/*
+ * sinkattn.h -- C ABI of libsinkattn: grouped-query flash attention with
+ * per-head learned attention sinks on AMD MI355X (gfx950).
+ *
+ * What is computed.  Perplexity blog "GPT-OSS on day 0" (French rendering
+ * "GPT-OSS au jour J"), sections "GPT-OSS on Hopper" (GQA with one pretrained
+ * sink per head, counted in the softmax) and "Kernels for GPT-OSS > Sink
+ * attention" (the sink is an extra term of the softmax next to the Q.K
+ * products; the streaming softmax keeps a running max m and a scale d, which
+ * start at the head's sink value and 1; when the KV sequence is split into
+ * blocks only the first block carries the sink).  For request b with n_q query
+ * rows and n_k cached keys, query row t, query head h, KV head g = h / (Hq/Hkv):
+ *
+ *   p    = n_k - n_q + t                      (bottom-right causal position)
+ *   keys = { j : lo <= j <= p },  lo = max(0, p - window + 1) if window > 0 else 0
+ *   Z    = exp(sink[h]) + sum_j exp(sm_scale * <q[t,h], k[j,g]>)
+ *   out  = sum_j exp(sm_scale * <q[t,h], k[j,g]>) / Z * v[j,g]
+ *   lse  = ln Z                              (natural log; includes the sink)
+ *
+ * The sink is on the scaled-logit scale (sm_scale never multiplies it) and
+ * has no value row.  A NULL sinks pointer means every sink is -inf, which is
+ * plain softmax attention.
+ *
+ * KV metadata.  "Accelerating Sonar through speculation" (Perplexity blog,
+ * Greek rendering), section "Inference with speculative decoding": the
+ * scheduler allocates KV-cache pages per request and the CPU builds the
+ * metadata (index pointers, page tables) that configures the attention
+ * kernel, then copies it to GPU memory.  Here that metadata is the
+ * sinkattn_kv descriptor below.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device memory unless documented "host".  bf16 tensors are
+ *    raw 16-bit patterns.  All tensors are dense, row-major, contiguous.
+ *  - Layouts: q and out [total_q, Hq, 64]; contiguous K/V [total_kv, Hkv, 64];
+ *    paged K/V pools [num_pages, Hkv, 16, 64] (one (page, KV head) block is
+ *    2 KiB contiguous); sinks [Hq] fp32; lse [total_q, Hq] fp32.
+ *  - Ownership: the caller allocates and owns every buffer.  The library
+ *    allocates no device memory, never synchronises the host, and keeps no
+ *    device state between calls; work is enqueued on `stream` (a hipStream_t,
+ *    NULL = the default stream) and is safe to capture in a HIP graph.
+ *  - Errors: argument problems are found on the host before anything is
+ *    enqueued, so a non-OK status means nothing was launched and nothing was
+ *    written.  SINKATTN_ERR_HIP reports a failed launch.  Device-resident
+ *    metadata (kv_len, page ids, index pointers) is trusted: it is not
+ *    validated, since that would need a host synchronisation.
+ *  - Thread safety: entry points may be called concurrently from several
+ *    host threads; sinkattn_last_error() is per thread.
+ *  - Supported shapes: head_dim 64, page_size 16, 1 <= Hq/Hkv <= 16,
+ *    Hq % Hkv == 0.
+ */
+#ifndef SINKATTN_H_
+#define SINKATTN_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SINKATTN_ABI_VERSION 1
+#define SINKATTN_HEAD_DIM 64
+#define SINKATTN_PAGE_SIZE 16
+#define SINKATTN_MAX_SPLITS 256
+
+typedef enum {
+  SINKATTN_OK = 0,
+  SINKATTN_ERR_INVALID_ARG = 1, /* NULL required pointer, Hq % Hkv != 0, batch < 1, bad split
+                                   count, window < 0, sm_scale not finite or <= 0 ... */
+  SINKATTN_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels implement: head_dim
+                                   != 64, page_size != 16, Hq/Hkv > 16 */
+  SINKATTN_ERR_HIP = 3          /* a kernel launch failed; sinkattn_last_error() has the text */
+} sinkattn_status;
+
+/* Where the keys and values of the batch live (a host struct holding device
+ * pointers).
+ *   paged == 0:  k, v are [total_kv, Hkv, 64] bf16; request b owns rows
+ *                kv_indptr[b] .. kv_indptr[b+1]-1, so n_k = kv_indptr[b+1] -
+ *                kv_indptr[b]; kv_len and page_indices are ignored.
+ *   paged == 1:  k, v are pools [num_pages, Hkv, 16, 64] bf16; request b's
+ *                logical key j lives in slot j % 16 of physical page
+ *                page_indices[kv_indptr[b] + j / 16]; n_k = kv_len[b].
+ *                Slots past a request's last key are never read.
+ *   kv_indptr [B+1] int32 and kv_len [B] int32 are device arrays; page ids are
+ *   int32 but byte offsets into the pools are computed in 64 bits. */
+typedef struct sinkattn_kv {
+  const void* k;
+  const void* v;
+  int32_t paged;
+  int32_t page_size;             /* paged: must be 16 */
+  const int32_t* kv_indptr;
+  const int32_t* page_indices;   /* paged only */
+  const int32_t* kv_len;         /* paged only */
+} sinkattn_kv;
+
+/* Causal or sliding-window prefill over a batch of requests, each with
+ * n_q >= 1 new query rows whose own keys are already in the cache (n_q <=
+ * n_k).  Chunked prefill and decode rows may be mixed in one call: rows of
+ * requests with n_q == 1 are handled by the decode kernel (two launches on
+ * `stream`).
+ *   q          [total_q, Hq, 64] bf16, request b's rows qo_indptr[b] .. qo_indptr[b+1]-1
+ *   qo_indptr  [batch+1] int32 (device)
+ *   kv         host pointer to the KV descriptor
+ *   sinks      [Hq] fp32 or NULL (no sink)
+ *   out        [total_q, Hq, 64] bf16, written
+ *   lse        [total_q, Hq] fp32 natural-log LSE (sink included), or NULL
+ *   total_q    number of query rows (= qo_indptr[batch]); sizes the launch
+ *   window     0 = full causal, W > 0 = each row sees its last W positions
+ *              (its own included) */
+sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const sinkattn_kv* kv,
+                                 const float* sinks, void* out, float* lse, int32_t batch,
+                                 int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, float sm_scale, int32_t window, void* stream);
+
+/* One query token per request over a paged KV cache, split along the KV
+ * sequence into num_splits chunks of whole pages: with n_pages =
+ * ceil(n_k / 16) and ppc = ceil(n_pages / num_splits), chunk c covers pages
+ * [c*ppc, min((c+1)*ppc, n_pages)) (chunks may be empty).  The sink enters
+ * chunk 0 only ("Kernels for GPT-OSS > Sink attention").  The query of
+ * request b sits at position kv_len[b] - 1.
+ *   q          [batch, Hq, 64] bf16
+ *   kv         paged descriptor (kv->paged must be 1)
+ *   num_splits 1 .. SINKATTN_MAX_SPLITS
+ *   out        num_splits == 1: [batch, Hq, 64] bf16 (required).
+ *              num_splits > 1: optional; when given, the partials are merged
+ *              into it by a second launch (same as calling sinkattn_merge).
+ *   o_part     num_splits > 1: [batch, Hq, num_splits, 64] fp32, each chunk
+ *              normalised by its own denominator; empty chunks hold 0.
+ *   lse_part   num_splits > 1: [batch, Hq, num_splits] fp32 natural-log
+ *              partial LSE: -inf for an empty chunk, the sink for an empty
+ *              chunk 0.  Both ignored (may be NULL) when num_splits == 1.
+ *   lse        optional [batch, Hq] fp32 final LSE (written with out). */
+sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                      int32_t num_splits, void* out, float* o_part,
+                                      float* lse_part, float* lse, int32_t batch,
+                                      int32_t num_qo_heads, int32_t num_kv_heads,
+                                      int32_t head_dim, float sm_scale, int32_t window,
+                                      void* stream);
+
+/* Log-sum-exp merge of split partials (the combination implied by splitting
+ * the softmax along the KV sequence): per (row, head), with M = max_c lse_c
+ * and w_c = exp(lse_c - M), out = sum_c w_c o_c / sum_c w_c and
+ * lse = M + ln sum_c w_c; all-(-inf) rows give out = 0, lse = -inf.
+ *   o_part [rows, num_heads, num_splits, 64] fp32, lse_part [rows, num_heads,
+ *   num_splits] fp32; out [rows, num_heads, 64] bf16; lse_out optional
+ *   [rows, num_heads] fp32. */
+sinkattn_status sinkattn_merge(const float* o_part, const float* lse_part, int32_t rows,
+                               int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
+                               float* lse_out, void* stream);
+
+/* Host-only: the chunk rule used by sinkattn_decode_paged, for callers and
+ * tests.  kv_len_host [batch] (host), bounds_host [batch, num_splits, 2]
+ * (host) receives each chunk's token range [lo, hi). */
+sinkattn_status sinkattn_split_bounds(const int32_t* kv_len_host, int32_t batch,
+                                      int32_t page_size, int32_t num_splits,
+                                      int32_t* bounds_host);
+
+/* Host-only: a split count for sinkattn_decode_paged chosen for the shape
+ * (kv_len_host [batch], host): enough (request, KV head, chunk) work units to
+ * fill the GPU without making chunks shorter than a few pages. */
+int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int32_t num_kv_heads);
+
+const char* sinkattn_status_string(sinkattn_status status);
+const char* sinkattn_last_error(void); /* message of this thread's last failing call */
+int32_t sinkattn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SINKATTN_H_ */

@@ -1,0 +1,154 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/sinkattn.h declares, its host-only split rule equals the oracle's, and
+argument errors come back as status codes before anything is launched."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gqa_attention_sinks_amd as sa
+import oracle
+from gqa_attention_sinks_amd import binding
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "sinkattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sa.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return sa.load_library()
+
+
+def _declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sinkattn_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_three_calls():
+    names = _declared_symbols()
+    for n in ["sinkattn_prefill", "sinkattn_decode_paged", "sinkattn_merge"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_symbols()
+    assert names, "no declarations parsed"
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/sinkattn.h but not exported"
+    assert set(names) == set(binding.EXPORTED)
+
+
+def test_abi_version(lib):
+    assert sa.abi_version() == 1
+    assert lib.sinkattn_status_string(0) == b"ok"
+    assert lib.sinkattn_status_string(2) == b"unsupported"
+
+
+def test_split_rule_matches_oracle_exactly(lib):
+    rng = np.random.default_rng(123)
+    all_lens = np.arange(0, 4097, dtype=np.int32)
+    for s in range(1, 17):
+        np.testing.assert_array_equal(sa.split_bounds(all_lens, s), oracle.split_bounds_ref(all_lens, s))
+    lens = rng.integers(0, 300000, size=100000).astype(np.int32)
+    for s in [1, 3, 16]:
+        np.testing.assert_array_equal(sa.split_bounds(lens, s), oracle.split_bounds_ref(lens, s))
+    for s in [37, 256]:
+        np.testing.assert_array_equal(sa.split_bounds(lens[:3000], s), oracle.split_bounds_ref(lens[:3000], s))
+    # long-context shape: 16 chunks of 8192 keys
+    b = sa.split_bounds([131072], 16)
+    assert np.all(b[0, :, 1] - b[0, :, 0] == 8192)
+
+
+def test_pick_num_splits_is_in_range(lib):
+    assert 1 <= sa.pick_num_splits(np.full(64, 4096), 8) <= 256
+    assert sa.pick_num_splits(np.full(8, 131072), 8) == 16
+    assert sa.pick_num_splits(np.full(4, 10), 8) == 1
+
+
+# ---------------------------------------------------------------------------
+# argument errors: every call below fails validation on the host, so no
+# kernel is launched and the fake device pointers are never touched.
+# ---------------------------------------------------------------------------
+
+FAKE = ctypes.c_void_p(0x1000)
+INVALID, UNSUPPORTED = 1, 2
+
+
+def _kv(paged=1, page_size=16, k=FAKE, page_indices=FAKE, kv_len=FAKE):
+    return binding._KV(k, FAKE, paged, page_size, FAKE, page_indices if paged else None,
+                       kv_len if paged else None)
+
+
+def _prefill(lib, kv, q=FAKE, qo=FAKE, out=FAKE, batch=2, total_q=4, hq=8, hkv=2, d=64, scale=0.125, window=0):
+    return lib.sinkattn_prefill(q, qo, ctypes.byref(kv) if kv is not None else None, None, out, None,
+                                batch, total_q, hq, hkv, d, ctypes.c_float(scale), window, None)
+
+
+def _decode(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, hq=8, hkv=2, d=64, scale=0.125,
+            window=0, q=FAKE):
+    return lib.sinkattn_decode_paged(q, ctypes.byref(kv) if kv is not None else None, None, s, out, o_part,
+                                     lse_part, None, batch, hq, hkv, d, ctypes.c_float(scale), window, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(batch=0), INVALID),
+    (dict(hq=6, hkv=4), INVALID),
+    (dict(d=128), UNSUPPORTED),
+    (dict(hq=64, hkv=2), UNSUPPORTED),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(window=-1), INVALID),
+    (dict(total_q=1), INVALID),
+])
+def test_prefill_argument_errors(lib, kwargs, code):
+    assert _prefill(lib, _kv(), **kwargs) == code
+    assert lib.sinkattn_last_error()
+
+
+def test_prefill_kv_errors(lib):
+    assert _prefill(lib, None) == INVALID
+    assert _prefill(lib, _kv(page_size=32)) == UNSUPPORTED
+    assert _prefill(lib, _kv(page_indices=None)) == INVALID
+    assert _prefill(lib, _kv(k=None)) == INVALID
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), INVALID),
+    (dict(s=0), INVALID),
+    (dict(s=257), INVALID),
+    (dict(s=1, out=None), INVALID),
+    (dict(s=4, o_part=None, lse_part=FAKE), INVALID),
+    (dict(s=4, o_part=FAKE, lse_part=None), INVALID),
+    (dict(d=32), UNSUPPORTED),
+    (dict(hq=7, hkv=2), INVALID),
+])
+def test_decode_argument_errors(lib, kwargs, code):
+    assert _decode(lib, _kv(), **kwargs) == code
+
+
+def test_decode_needs_paged(lib):
+    assert _decode(lib, _kv(paged=0)) == INVALID
+
+
+def test_merge_argument_errors(lib):
+    m = lib.sinkattn_merge
+    assert m(None, FAKE, 4, 8, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 0, 8, 2, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 4, 8, 0, 64, FAKE, None, None) == INVALID
+    assert m(FAKE, FAKE, 4, 8, 2, 80, FAKE, None, None) == UNSUPPORTED
+
+
+def test_split_bounds_argument_errors(lib):
+    out = np.zeros(8, dtype=np.int32)
+    lens = np.array([5], dtype=np.int32)
+    f = lib.sinkattn_split_bounds
+    assert f(None, 1, 16, 2, out.ctypes.data_as(ctypes.c_void_p)) == INVALID
+    assert f(lens.ctypes.data_as(ctypes.c_void_p), 1, 16, 0, out.ctypes.data_as(ctypes.c_void_p)) == INVALID

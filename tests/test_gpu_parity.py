@@ -1,0 +1,215 @@
+"""GPU parity: the HIP library (through its C ABI binding) against the fp64
+oracle on the same seeded inputs.
+
+What is being checked (Perplexity blog "GPT-OSS on day 0", section "Kernels
+for GPT-OSS > Sink attention"): one sink logit per head in the softmax
+denominator with no value row, the streaming softmax seeded with it, and under
+a KV split the sink in the first chunk only.
+
+Sizes: small cases compare every element; the GPT-OSS-shaped workloads run at
+their full sizes in the launch configuration the benchmark times, compared
+element by element where the oracle finishes in seconds (decode) and on
+sampled rows otherwise (prefill).
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from gqa_attention_sinks_amd import workloads as wl
+from tests._gpu import (DeviceWorkload, assert_parity, kv_cache, oracle_full, oracle_rows, say,
+                        to_host)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sinks_amd as sa
+    sa.load_library()
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+
+def test_tiny_prefill_full():
+    w = wl.tiny_prefill()
+    say("tiny_prefill: B=1 Hq=4 Hkv=1 n=128 contiguous")
+    d = DeviceWorkload(w)
+    out, lse = d.prefill(window=0)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, "tiny_prefill", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("window", [0, 1, 37, 128, 129])
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_ragged_small(window, paged):
+    """Ragged requests spanning several tiles, chunked prefill (n_q < n_k),
+    GQA 8:1, windows around a tile edge, paged and contiguous KV."""
+    rng = np.random.default_rng(11)
+    kv_len = np.array([1, 130, 300, 77, 513])
+    qo_len = np.array([1, 130, 129, 20, 257])
+    maker = wl.make_paged if paged else wl.make_contiguous
+    w = maker("ragged", kv_len, qo_len, 16, 2, rng=rng)
+    say(f"prefill ragged paged={paged} window={window} qo={list(qo_len)} kv={list(kv_len)}")
+    out, lse = DeviceWorkload(w).prefill(window=window)
+    ro, rl = oracle_full(w, window)
+    assert_parity(to_host(out), ro, f"prefill ragged w={window} paged={paged}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("group", [1, 4, 16])
+def test_prefill_group_sizes_and_no_sinks(group):
+    rng = np.random.default_rng(12 + group)
+    hkv = 2
+    w = wl.make_contiguous("groups", [200, 64], [200, 33], hkv * group, hkv, rng=rng)
+    say(f"prefill group={group}")
+    d = DeviceWorkload(w)
+    out, lse = d.prefill(window=0)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, f"prefill group {group}", to_host(lse), rl)
+    out, lse = d.prefill(window=0, sinks=False)
+    ro, rl = oracle_full(w, 0, sinks=False)
+    assert_parity(to_host(out), ro, f"prefill group {group} no sinks", to_host(lse), rl)
+
+
+def test_prefill_outlier_sinks():
+    rng = np.random.default_rng(13)
+    w = wl.make_paged("outliers", [300, 64], [300, 64], 16, 2, rng=rng, sink_overrides=wl.outlier_sinks)
+    say("prefill with -inf / +20 sinks")
+    out, lse = DeviceWorkload(w).prefill(window=0)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, "prefill outlier sinks", to_host(lse), rl)
+
+
+def _sample_rows(w, per_request, rng):
+    rows = []
+    for b in range(w.batch):
+        lo, hi = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        n = hi - lo
+        pick = {0, n - 1, min(n - 1, 127), min(n - 1, 128)}
+        pick.update(rng.integers(0, n, size=per_request).tolist())
+        rows.extend(lo + t for t in sorted(pick))
+    return np.array(rows)
+
+
+def test_causal_prefill_full_size_sampled():
+    """4 x 8192 causal prefill, 64/8 heads: full launch, sampled rows checked."""
+    w = wl.causal_prefill()
+    say("causal_prefill full size: B=4 n=8192 Hq=64 Hkv=8")
+    out, lse = DeviceWorkload(w).prefill(window=0)
+    rows = _sample_rows(w, 12, np.random.default_rng(5))
+    g, gl = to_host(out)[rows], to_host(lse)[rows]
+    ro, rl = oracle_rows(w, rows, 0)
+    assert_parity(g, ro, "causal_prefill sampled rows", gl, rl)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits", [1, 2, 5, 16])
+def test_paged_decode_full(num_splits):
+    w = wl.paged_decode()
+    say(f"paged_decode full size: B=64 kv~U[1,4096] S={num_splits}")
+    d = DeviceWorkload(w)
+    out, lse = d.decode(num_splits)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, f"paged_decode S={num_splits}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("length", [1, 15, 16, 17, 4095, 4096])
+@pytest.mark.parametrize("window", [0, 1, 127, 128, 129])
+def test_decode_edge_lengths_windows(length, window):
+    rng = np.random.default_rng(length * 7 + window)
+    w = wl.make_paged("edge", [length, max(1, length // 2)], [1, 1], 16, 2, rng=rng, decode=True,
+                      sink_overrides=wl.outlier_sinks)
+    say(f"decode edge length={length} window={window}")
+    d = DeviceWorkload(w)
+    ro, rl = oracle_full(w, window)
+    for s in [1, 3, 16]:
+        out, lse = d.decode(s, window=window)
+        assert_parity(to_host(out), ro, f"decode L={length} W={window} S={s}", to_host(lse), rl)
+
+
+def test_decode_partials_sink_only_in_chunk_zero():
+    """The partials themselves: chunk 0 carries the sink, the others do not."""
+    w = wl.paged_decode(batch=6, max_len=700)
+    w.sinks = wl.outlier_sinks(w.sinks)
+    say("decode partials S=4")
+    o_part, lse_part = DeviceWorkload(w).decode(4, merge=False)
+    ro, rl = oracle.split_partials_ref(w.q, kv_cache(w), w.sinks, w.scale, 4)
+    assert_parity(to_host(o_part), ro, "o_part", to_host(lse_part), rl)
+
+
+def test_long_split_decode_full_size():
+    """8 x 131072 keys, 16 chunks, sinks with -inf and +20 outliers."""
+    w = wl.long_split_decode()
+    say("long_split_decode full size: B=8 L=131072 S=16")
+    d = DeviceWorkload(w)
+    o_part, lse_part = d.decode(16, merge=False)
+    out, lse = d.decode(16)
+    kv = kv_cache(w)
+    rp, rlp = oracle.split_partials_ref(w.q, kv, w.sinks, w.scale, 16, workers=8)
+    assert_parity(to_host(o_part), rp, "long decode partials", to_host(lse_part), rlp)
+    ro, rl = oracle.merge_ref(rp, rlp)
+    assert_parity(to_host(out), ro, "long decode merged", to_host(lse), rl)
+
+
+# ---------------------------------------------------------------------------
+# mixed batch
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_mixed_batch_small_full(window):
+    w = wl.mixed_batch(n_prefill=4, chunk=200, max_prefix=900, n_decode=30, max_decode_len=1500)
+    say(f"mixed small window={window}")
+    out, lse = DeviceWorkload(w).prefill(window=window)
+    ro, rl = oracle_full(w, window)
+    assert_parity(to_host(out), ro, f"mixed small W={window}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("window", [128, 0])
+def test_mixed_batch_full_size(window):
+    """16 x 512-token prefill chunks + 240 decode rows in one call: every decode
+    row checked, prefill rows sampled."""
+    w = wl.mixed_batch()
+    say(f"mixed_batch full size window={window}")
+    out, lse = DeviceWorkload(w).prefill(window=window)
+    n_pre = w.meta["n_prefill"]
+    dec_rows = np.arange(int(w.qo_indptr[n_pre]), w.total_q)
+    rng = np.random.default_rng(9)
+    pre_rows = []
+    for b in range(n_pre):
+        lo = int(w.qo_indptr[b])
+        pre_rows += [lo, lo + 127, lo + 128, lo + 511] + (lo + rng.integers(0, 512, 4)).tolist()
+    rows = np.concatenate([np.array(pre_rows), dec_rows])
+    g, gl = to_host(out)[rows], to_host(lse)[rows]
+    ro, rl = oracle_rows(w, rows, window)
+    assert_parity(g, ro, f"mixed full W={window}", gl, rl)
+
+
+# ---------------------------------------------------------------------------
+# merge entry point
+# ---------------------------------------------------------------------------
+
+def test_merge_entry_point():
+    import torch
+    import gqa_attention_sinks_amd as sa
+    rng = np.random.default_rng(3)
+    rows, heads, s = 5, 8, 7
+    o = rng.normal(size=(rows, heads, s, 64)).astype(np.float32)
+    l = rng.normal(0, 3, size=(rows, heads, s)).astype(np.float32)
+    l[0, 0, :] = -np.inf
+    o[0, 0, :] = 0
+    l[1, :, 3:] = -np.inf
+    l[2, 1, 0] = 40.0
+    say("merge entry point")
+    dev = torch.device("cuda:0")
+    out, lse = sa.merge(torch.from_numpy(o).to(dev), torch.from_numpy(l).to(dev), return_lse=True)
+    ro, rl = oracle.merge_ref(o, l)
+    assert_parity(to_host(out)[1:], ro[1:], "merge", to_host(lse), rl)
+    assert np.all(to_host(out)[0, 0] == 0)

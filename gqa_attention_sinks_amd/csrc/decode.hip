@@ -16,10 +16,12 @@
 //       (the G <= 16 query heads sharing KV head g are the MFMA columns; K goes
 //        straight from HBM into the A operand, one 32-byte run per lane)
 //     online softmax in base 2 on the accumulator (each lane: one head, 4 keys)
-//     O^T[64 dims x 16 heads] += V^T . P^T                 -> 4 x MFMA 16x16x16 bf16
-//       (P^T is the S^T accumulator converted in place; V is staged in LDS in
-//        its natural [key][dim] layout and read back transposed with
-//        ds_read_b64_tr_b16)
+//     O^T[64 dims x 16 heads] += V^T . P^T                 -> 4 x MFMA 16x16x16 fp16
+//       (P^T is the S^T accumulator converted in place to fp16; V is converted
+//        to fp16 and staged in LDS in its natural [key][dim] layout, then read
+//        back transposed with ds_read_b64_tr_b16).  The fp16 weights are taken
+//        relative to the running key maximum; the sink is folded in at the end,
+//        which gives exactly the state of the sink-seeded recurrence.
 //   Each chunk's result is normalised by its own denominator and written as an
 //   fp32 partial with its natural-log LSE, or, unsplit, as the bf16 output.
 
@@ -100,13 +102,11 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     q1 = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
   }
 
-  // Streaming state (base 2).  Chunk 0 starts from the sink: m = sink*log2(e)
-  // and d = 1, the 1 held by one lane of the head's four lanes.
+  // Key-domain streaming state (base 2): running key max, this lane's part of
+  // the denominator, P.V accumulator.  The sink of chunk 0 is folded in once
+  // the waves have merged (fold_sink), giving the state that the recurrence
+  // seeded with (m, d) = (sink, 1) holds after the same keys.
   float m = kNegInf, dsum = 0.f;
-  if (c == 0 && wave == 0 && head_ok && a.sinks != nullptr) {
-    m = a.sinks[head] * kLog2e;
-    dsum = grp == 0 ? 1.f : 0.f;
-  }
   f32x4 acc[4] = {};
 
   const int32_t* pages = a.page_indices + a.page_indptr[b];
@@ -173,14 +173,19 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) p[i] = exp2_hw(s[u][i] - m_use);
-      const uint32_t p01 = pack_bf16x2(p[0], p[1]);
-      const uint32_t p23 = pack_bf16x2(p[2], p[3]);
-      dsum = add_bf16x2(p23, add_bf16x2(p01, dsum));
-      const i16x4 pb = __builtin_bit_cast(i16x4, u32x2{p01, p23});
+      const uint32_t p01 = pack_f16x2(p[0], p[1]);
+      const uint32_t p23 = pack_f16x2(p[2], p[3]);
+      dsum = add_f16x2(p23, add_f16x2(p01, dsum));
+      const f16x4 pb = __builtin_bit_cast(f16x4, u32x2{p01, p23});
 
       // stage V (natural layout, swizzled); rows past the last key are zeroed
       // so that no stale or poisoned value can meet a zero weight.
-      u32x4 v0 = vc[u][0], v1 = vc[u][1];
+      u32x4 v0, v1;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v0[e] = bf16x2_to_f16x2(vc[u][0][e]);
+        v1[e] = bf16x2_to_f16x2(vc[u][1][e]);
+      }
       if ((lp + u) * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
       uint8_t* buf = stage + u * kPageBytes;
       *reinterpret_cast<u32x4*>(buf + page_swizzle(col, 2 * grp)) = v0;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
         const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
                 reinterpret_cast<uintptr_t>(buf + byte)));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vt, pb, acc[db], 0, 0, 0);
+        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt), pb, acc[db], 0, 0, 0);
       }
       __asm__ volatile("" ::: "memory");
     }
@@ -226,20 +231,24 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   for (int idx = threadIdx.x; idx < a.group * kHeadDim; idx += NW * 64) {
     const int hh = idx / kHeadDim;
     const int d = idx % kHeadDim;
+    const int h = g * a.group + hh;
     float mx = kNegInf;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * 16 + hh]);
     float den = 0.f, num = 0.f;
+    if (mx != kNegInf) {
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w * 16 + hh];
-      const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
-      den += wt * sm_d[w * 16 + hh];
-      num += wt * sm_o[(w * 16 + hh) * kHeadDim + d];
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w * 16 + hh];
+        const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
+        den += wt * sm_d[w * 16 + hh];
+        num += wt * sm_o[(w * 16 + hh) * kHeadDim + d];
+      }
     }
-    const float o = den > 0.f ? num / den : 0.f;
-    const float lse_nat = (mx + log2_hw(den)) * kLn2;   // -inf when den == 0
-    const int h = g * a.group + hh;
+    const float sink2 = (c == 0 && a.sinks != nullptr) ? a.sinks[h] * kLog2e : kNegInf;
+    float lse2;
+    const float o = num * fold_sink(sink2, mx, den, &lse2);
+    const float lse_nat = lse2 * kLn2;
     if (S == 1) {
       a.out[((size_t)qrow * a.num_qo_heads + h) * kHeadDim + d] = to_bf16_bits(o);
       if (a.lse != nullptr && d == 0) a.lse[(size_t)qrow * a.num_qo_heads + h] = lse_nat;

@@ -16,9 +16,13 @@
 //     S^T[64 keys x 32 rows] = K . Q^T    -> 8 x MFMA 32x32x16 bf16 (Q^T in registers)
 //     base-2 online softmax on the accumulator: each lane holds one query row
 //     and 32 of its keys, so the row max needs one exchange with lane ^ 32
-//     O^T[64 dims x 32 rows] += V^T . P^T -> 8 x MFMA 32x32x16 bf16
-//       (P^T is the converted score accumulator; V^T comes from the natural
-//        [key][dim] LDS tile through ds_read_b64_tr_b16)
+//     O^T[64 dims x 32 rows] += V^T . P^T -> 8 x MFMA 32x32x16 fp16
+//       (P^T is the score accumulator converted to fp16; V is converted to
+//        fp16 once when its tile is staged, and V^T comes from the natural
+//        [key][dim] LDS tile through ds_read_b64_tr_b16).  fp16 weights carry
+//        three more mantissa bits than bf16; they are taken relative to the
+//        running key maximum and the sink is folded in at the end, which
+//        gives exactly the state of the sink-seeded recurrence.
 //   Masking is applied only on tiles that cross the causal diagonal or the
 //   window's lower edge.
 
@@ -149,11 +153,10 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
       qop[ks] = ok ? __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks)) : bf16x8{};
   }
 
+  // key-domain streaming state: running key max (base 2), partial
+  // denominator of this lane's keys, P.V accumulator; the sink is folded in
+  // at the end (fold_sink), giving the state the sink-seeded recurrence holds
   float m = kNegInf, dsum = 0.f;
-  if (a.sinks != nullptr) {
-    m = a.sinks[head] * kLog2e;
-    dsum = half == 0 ? 1.f : 0.f;
-  }
   f32x16 acc[2] = {};
 
   // tile loader: thread -> (key = tid / 4, 32 bytes at dims 16 * (tid % 4))
@@ -185,8 +188,14 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
     uint8_t* vs = ks + kTileBytes;
     *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c)) = kr[0];
     *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c + 1)) = kr[1];
-    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c)) = vr[0];
-    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c + 1)) = vr[1];
+    // V is staged as fp16: the weights of the P.V product are fp16
+    u32x4 v16[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v16[u][e] = bf16x2_to_f16x2(vr[u][e]);
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c)) = v16[0];
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c + 1)) = v16[1];
   };
 
   {
@@ -248,8 +257,8 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[db][i] *= alpha;
 
-      // P^T operands: MFMA r covers keys 16r .. 16r+15 of the tile
-      bf16x8 pop[4];
+      // P^T operands (fp16): MFMA r covers keys 16r .. 16r+15 of the tile
+      f16x8 pop[4];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -258,13 +267,13 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
           for (int e = 0; e < 8; ++e) p[e] = exp2_hw(__builtin_fmaf(s[kb][8 * hh + e], a.scale_log2, -m_use));
           u32x4 pk;
-          pk[0] = pack_bf16x2(p[0], p[1]);
-          pk[1] = pack_bf16x2(p[2], p[3]);
-          pk[2] = pack_bf16x2(p[4], p[5]);
-          pk[3] = pack_bf16x2(p[6], p[7]);
+          pk[0] = pack_f16x2(p[0], p[1]);
+          pk[1] = pack_f16x2(p[2], p[3]);
+          pk[2] = pack_f16x2(p[4], p[5]);
+          pk[3] = pack_f16x2(p[6], p[7]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) dsum = add_bf16x2(pk[e], dsum);
-          pop[2 * kb + hh] = __builtin_bit_cast(bf16x8, pk);
+          for (int e = 0; e < 4; ++e) dsum = add_f16x2(pk[e], dsum);
+          pop[2 * kb + hh] = __builtin_bit_cast(f16x8, pk);
         }
 
       // O^T += V^T . P^T ; V^T rows from transposed LDS reads
@@ -280,7 +289,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_b, chunk) + sub));
           typedef __attribute__((ext_vector_type(8))) short i16x8;
           const i16x8 both = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, both), pop[r], acc[db], 0, 0, 0);
+          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, both), pop[r], acc[db], 0, 0, 0);
         }
       }
     }
@@ -292,7 +301,9 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
   if (!wave_live) return;
   dsum += shfl_xor_f32(dsum, 32);
   if (my_t >= n_q) return;
-  const float inv = dsum > 0.f ? 1.f / dsum : 0.f;
+  const float sink2 = a.sinks != nullptr ? a.sinks[head] * kLog2e : kNegInf;
+  float lse2;
+  const float inv = fold_sink(sink2, m, dsum, &lse2);
   const size_t orow = ((size_t)(q_begin + my_t) * a.num_qo_heads + head) * kHeadDim;
 #pragma unroll
   for (int db = 0; db < 2; ++db)
@@ -305,7 +316,7 @@ __global__ __launch_bounds__(kWaves * 64) void prefill_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x2*>(a.out + orow + d0) = w;
     }
   if (a.lse != nullptr && half == 0)
-    a.lse[(size_t)(q_begin + my_t) * a.num_qo_heads + head] = (m + log2_hw(dsum)) * kLn2;
+    a.lse[(size_t)(q_begin + my_t) * a.num_qo_heads + head] = lse2 * kLn2;
 }
 
 }  // namespace

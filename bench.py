@@ -1,0 +1,324 @@
+#!/usr/bin/env python3
+"""Benchmark of the sink-attention hot path on one MI355X.
+
+Default run (one JSON line on stdout):
+  * headline: paged split-KV decode, 64 requests with KV lengths uniform in
+    [1, 4096], 64 query / 8 KV heads, head_dim 64, page size 16, pages
+    permuted in a shared pool, sinks N(0, 2).  One step = one whole pass of
+    the decode path: per-(request, KV head, chunk) split decode (chunk bounds
+    computed on the device, paged gather, scores, mask, streaming softmax
+    with the sink in chunk 0, P.V, partials) followed by the LSE merge.
+    ``value`` = algorithmic HBM bytes / step time (GB/s), inputs resident in
+    HBM, three replicas of the KV pool rotated so no step finds its KV in the
+    256 MB Infinity Cache.
+  * ``roofline``: the decode kernel alone, timed with HIP events on the
+    stream it runs on, against 8 TB/s.
+  * ``prefill``: causal prefill, 4 x 8192 tokens, 64/8 heads: TFLOP/s of
+    4 * head_dim flops per visible (query, key, head) against 2.5 PFLOP/s.
+  * ``cpu_baseline``: the fp64 oracle on the host, timed on the whole decode
+    workload, plus the parity of the timed GPU output against it.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, vendor spec
+METRIC = "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), oracle-matched"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=100)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--splits", type=int, default=0, help="decode split count (0: library's pick)")
+    p.add_argument("--replicas", type=int, default=3)
+    p.add_argument("--prefill-steps", type=int, default=20)
+    p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--workload", default="paged_decode",
+                   choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill"],
+                   help="for profiling runs: time only this workload")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+
+def decode_bytes(w):
+    """K + V of every live key once per KV head, + Q + out + metadata."""
+    kv = int(np.sum(w.kv_len, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * 2
+    qo = 2 * w.batch * w.num_qo_heads * w.head_dim * 2
+    meta = 4 * (len(w.page_indices) + 2 * w.batch + 1)
+    return kv + qo + meta
+
+
+def prefill_flops(w, window=0):
+    """4 * head_dim per visible (query, key, head)."""
+    vis = 0
+    for b in range(w.batch):
+        n_q, n_k = int(w.qo_len[b]), int(w.kv_len[b])
+        p = n_k - n_q + np.arange(n_q, dtype=np.int64)
+        lo = np.maximum(0, p - window + 1) if window > 0 else np.zeros_like(p)
+        vis += int(np.sum(p - lo + 1))
+    return 4 * w.head_dim * vis * w.num_qo_heads
+
+
+# ---------------------------------------------------------------------------
+# GPU runs
+# ---------------------------------------------------------------------------
+
+class Dev:
+    def __init__(self, w, torch, dev):
+        def bits(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+        self.q = bits(w.q)
+        self.qo_indptr = i32(w.qo_indptr)
+        self.k = bits(w.k)
+        self.v = bits(w.v)
+        self.kv_indptr = i32(w.kv_indptr)
+        self.kv_len = i32(w.kv_len)
+        self.page_indices = i32(w.page_indices) if w.paged else None
+        self.sinks = torch.from_numpy(w.sinks).to(dev)
+
+    def replica(self):
+        r = Dev.__new__(Dev)
+        r.__dict__ = {k: (v.clone() if v is not None else None) for k, v in self.__dict__.items()}
+        return r
+
+
+def time_decode(w, args, torch, dev):
+    """Decode + merge steps through the C ABI with prebuilt arguments (the
+    Python binding's checks would otherwise cost more than a step)."""
+    import ctypes
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import binding
+    lib = sa.load_library()
+    base = Dev(w, torch, dev)
+    reps = [base] + [base.replica() for _ in range(max(0, args.replicas - 1))]
+    s = args.splits if args.splits > 0 else (w.num_splits or sa.pick_num_splits(w.kv_len, w.num_kv_heads))
+    B, H, HKV = w.batch, w.num_qo_heads, w.num_kv_heads
+    outs = [torch.empty_like(r.q) for r in reps]
+    o_part = torch.empty((B, H, s, 64), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((B, H, s), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len) for r in reps]
+    qp = [P(r.q.data_ptr()) for r in reps]
+    sk = [P(r.sinks.data_ptr()) for r in reps]
+    op = [P(o.data_ptr()) for o in outs]
+    opart, lpart, lsep = P(o_part.data_ptr()), P(lse_part.data_ptr()), P(lse.data_ptr())
+    scale = ctypes.c_float(w.scale)
+
+    def step(i, ev=None):
+        r = i % len(reps)
+        if ev is not None:
+            ev[0].record(stream)
+        if s > 1:
+            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
+                                           B, H, HKV, 64, scale, 0, sp)
+            if ev is not None:
+                ev[1].record(stream)
+            st |= lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lsep, sp)
+        else:
+            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lsep,
+                                           B, H, HKV, 64, scale, 0, sp)
+            if ev is not None:
+                ev[1].record(stream)
+        if ev is not None:
+            ev[2].record(stream)
+        if st != 0:
+            raise RuntimeError(lib.sinkattn_last_error().decode())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    last = (args.steps - 1) % len(reps)
+    out_host = outs[last].float().cpu().numpy().astype(np.float64)
+    # per-kernel durations with events on the launch stream (separate pass)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    mer_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    return dict(step_ms=wall * 1e3, decode_ms=dec_ms, merge_ms=mer_ms, splits=s, out=out_host)
+
+
+def time_prefill(w, steps, warmup, torch, dev, window=0):
+    from gqa_attention_sinks_amd import binding
+    d = Dev(w, torch, dev)
+    out = torch.empty_like(d.q)
+    stream = torch.cuda.current_stream()
+
+    def call():
+        binding.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale, window=window,
+                        page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    return dict(step_ms=wall * 1e3, kernel_ms=e0.elapsed_time(e1) / steps, out=out)
+
+
+def parity(g, r):
+    err = np.abs(g - r)
+    return dict(max_abs=float(err.max()), within_tol=bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r))))
+
+
+def cpu_baseline(w, gpu_out):
+    """The fp64 oracle (as it stands) on the whole decode workload, one thread."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    kv = oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr, paged=True, page_indices=w.page_indices,
+                        kv_len=w.kv_len)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        ro, _ = oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, 0, workers=1)
+        dt = time.perf_counter() - t0
+    return dict(value=decode_bytes(w) / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys), fp64 numpy, "
+                       f"{dt:.2f} s", seconds=dt), parity(gpu_out, ro)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sharded layout is described "
+              "in DESIGN.md and not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import workloads as wl
+    if not os.path.exists(sa.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    sa.load_library()
+    dev = torch.device("cuda:0")
+
+    if args.workload not in ("paged_decode",):
+        return profile_only(args, torch, dev, wl)
+
+    log("generating paged_decode workload")
+    w = wl.paged_decode()
+    res = time_decode(w, args, torch, dev)
+    nbytes = decode_bytes(w)
+    value = nbytes / (res["step_ms"] * 1e-3) / 1e9
+    achieved = nbytes / (res["decode_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "paged decode: batch 64, one query token each, KV lengths uniform in [1, 4096], "
+                        "64 query / 8 KV heads, head_dim 64, page size 16, pages permuted in a shared pool, "
+                        "sinks N(0, 2), seed 0",
+            "num_splits": res["splits"],
+            "kv_replicas_rotated": args.replicas,
+            "algorithmic_bytes": nbytes,
+            "compute": "bf16 Q.K^T and fp16 P.V on MFMA, fp32 accumulation",
+            "decode_kernel_ms": round(res["decode_ms"], 5),
+            "merge_kernel_ms": round(res["merge_ms"], 5),
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "decode_paged_kernel",
+        },
+    }
+    if not args.no_prefill:
+        log("generating causal_prefill workload")
+        wp = wl.causal_prefill()
+        pr = time_prefill(wp, args.prefill_steps, 3, torch, dev)
+        flops = prefill_flops(wp)
+        tflops = flops / (pr["kernel_ms"] * 1e-3) / 1e12
+        line["prefill"] = {
+            "workload": "causal prefill: batch 4 x 8192 tokens, 64 query / 8 KV heads, head_dim 64, contiguous KV, "
+                        "sinks N(0, 2)",
+            "value": round(tflops, 1),
+            "unit": "TFLOP/s",
+            "ms_per_call": round(pr["kernel_ms"], 4),
+            "algorithmic_flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "prefill_kernel"},
+        }
+        del pr
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        cb, par = cpu_baseline(w, res["out"])
+        line["cpu_baseline"] = {k: v for k, v in cb.items() if k != "seconds"}
+        line["parity"] = par
+    print(json.dumps(line), flush=True)
+
+
+def profile_only(args, torch, dev, wl):
+    """Time one named workload only (for rocprofv3 runs)."""
+    w = getattr(wl, args.workload)()
+    log(f"timing {args.workload}")
+    if args.workload == "long_split_decode":
+        res = time_decode(w, args, torch, dev)
+        gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9
+        print(json.dumps({"workload": args.workload, "step_ms": res["step_ms"], "decode_ms": res["decode_ms"],
+                          "merge_ms": res["merge_ms"], "decode_GBs": gbs, "frac": gbs / HBM_PEAK_GBS}))
+        return
+    for window in w.windows:
+        pr = time_prefill(w, args.steps, args.warmup, torch, dev, window=window)
+        flops = prefill_flops(w, window)
+        print(json.dumps({"workload": args.workload, "window": window, "ms": pr["kernel_ms"],
+                          "TFLOPs": flops / (pr["kernel_ms"] * 1e-3) / 1e12}))
+
+
+if __name__ == "__main__":
+    main()

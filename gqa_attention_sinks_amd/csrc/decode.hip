@@ -25,6 +25,9 @@
 //   Each chunk's result is normalised by its own denominator and written as an
 //   fp32 partial with its natural-log LSE, or, unsplit, as the bf16 output.
 
+#include <stdio.h>
+#include <stdlib.h>
+
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
@@ -56,7 +59,8 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, PPI>::kBytes];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // uniform per wave: keeps the page bookkeeping (and the page-id loads) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15;   // MFMA column (query head) or row (key) index
   const int grp = lane >> 4;   // 16-lane group
   const int S = a.num_splits;
@@ -112,29 +116,47 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const int32_t* pages = a.page_indices + a.page_indptr[b];
   const size_t head_stride = (size_t)kPageSize * kHeadDim;          // elements per (page, KV head)
   const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
-  const uint16_t* kbase = a.k_pool + (size_t)g * head_stride + col * kHeadDim + 16 * grp;
-  const uint16_t* vbase = a.v_pool + (size_t)g * head_stride + col * kHeadDim + 16 * grp;
+  const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
+  const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
+  const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block
   uint8_t* stage = smem + wave * (PPI * kPageBytes);
 
-  // register double buffer: pages of the current and the next step
+  // Page ids go through the scalar cache one step before their pages are
+  // fetched, so no vector-memory wait ever blocks on an id while K/V loads
+  // are in flight; K/V of the next step are loaded into registers while the
+  // current step computes.
+  int ids[PPI];
+  auto fetch_ids = [&](int lp) {
+#pragma unroll
+    for (int u = 0; u < PPI; ++u) ids[u] = (lp + u < wp1) ? pages[lp + u] : 0;
+  };
   u32x4 kc[PPI][2], vc[PPI][2];
   auto load_step = [&](int lp, u32x4 (&kr)[PPI][2], u32x4 (&vr)[PPI][2]) {
 #pragma unroll
     for (int u = 0; u < PPI; ++u) {
       if (lp + u < wp1) {
-        const size_t off = (size_t)pages[lp + u] * page_stride;
-        kr[u][0] = ldg16(kbase + off);
-        kr[u][1] = ldg16(kbase + off + 8);
-        vr[u][0] = ldg16(vbase + off);
-        vr[u][1] = ldg16(vbase + off + 8);
+        const size_t off = (size_t)ids[u] * page_stride;
+        const uint16_t* kp = kpool + off + lane_off;
+        const uint16_t* vp = vpool + off + lane_off;
+        kr[u][0] = ldg16(kp);
+        kr[u][1] = ldg16(kp + 8);
+        vr[u][0] = ldg16(vp);
+        vr[u][1] = ldg16(vp + 8);
       }
     }
   };
-  if (wp0 < wp1) load_step(wp0, kc, vc);
+  fetch_ids(wp0);
+  if (wp0 < wp1) {
+    load_step(wp0, kc, vc);
+    fetch_ids(wp0 + PPI);
+  }
 
   for (int lp = wp0; lp < wp1; lp += PPI) {
     u32x4 kn[PPI][2], vn[PPI][2];
-    if (lp + PPI < wp1) load_step(lp + PPI, kn, vn);
+    if (lp + PPI < wp1) {
+      load_step(lp + PPI, kn, vn);
+      fetch_ids(lp + 2 * PPI);
+    }
 
     // scores of PPI pages
     float s[PPI][4];
@@ -286,12 +308,37 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
+// Launch shapes: (waves per workgroup, pages per step).  SINKATTN_DECODE_SHAPE
+// ("4x2", "8x4", ...) overrides the default for tuning runs.
+struct DecodeShape { int nw, ppi; };
+
+static DecodeShape decode_shape() {
+  static const DecodeShape shape = [] {
+    DecodeShape d{4, 1};
+    if (const char* e = getenv("SINKATTN_DECODE_SHAPE")) {
+      int nw = 0, ppi = 0;
+      if (sscanf(e, "%dx%d", &nw, &ppi) == 2) d = DecodeShape{nw, ppi};
+    }
+    return d;
+  }();
+  return shape;
+}
+
+template <int NW, int PPI>
+static void launch_shape(const DecodeArgs& a, long units, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_paged_kernel<NW, PPI>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
+}
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const long units = (long)a.batch * a.num_kv_heads * a.num_splits;
   if (units <= 0) return hipSuccess;
-  constexpr int NW = 4, PPI = 2;
-  hipLaunchKernelGGL((decode_paged_kernel<NW, PPI>), dim3((unsigned)units), dim3(NW * 64), 0,
-                     stream, a);
+  const DecodeShape d = decode_shape();
+  if (d.nw == 2 && d.ppi == 4) launch_shape<2, 4>(a, units, stream);
+  else if (d.nw == 4 && d.ppi == 1) launch_shape<4, 1>(a, units, stream);
+  else if (d.nw == 4 && d.ppi == 4) launch_shape<4, 4>(a, units, stream);
+  else if (d.nw == 8 && d.ppi == 2) launch_shape<8, 2>(a, units, stream);
+  else if (d.nw == 8 && d.ppi == 4) launch_shape<8, 4>(a, units, stream);
+  else launch_shape<4, 2>(a, units, stream);
   return hipGetLastError();
 }
 

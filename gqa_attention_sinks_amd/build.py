@@ -23,8 +23,18 @@ ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: the softmax reads and rescales them with VALU ops
+    "-mllvm", "--amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
 ]
+
+
+# Kernel files only: the kernels never feed a NaN to min/max (masked scores are
+# -inf and rows past the last key are zero-filled), so max chains compile to
+# v_max3 without NaN canonicalisation.  The host validation in api.hip keeps
+# full NaN semantics (it must reject a NaN softmax scale).
+KERNEL_SOURCES = {"decode.hip", "prefill.hip"}
+KERNEL_FLAGS = ["-fno-honor-nans"]
 
 
 def hipcc() -> str:
@@ -43,23 +53,26 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
+    """Compile every source and link ``out``; ``extra_flags`` (e.g. -D tuning
+    switches) go to every compile."""
+    os.makedirs(build_dir, exist_ok=True)
     cc = hipcc()
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-        out = _run([cc, *FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+        flags = FLAGS + (KERNEL_FLAGS if src in KERNEL_SOURCES else [])
+        out = _run([cc, *flags, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
         if verbose and out.strip():
             print(out)
         return obj
 
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

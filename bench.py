@@ -177,9 +177,12 @@ def time_prefill(w, steps, warmup, torch, dev, window=0):
     out = torch.empty_like(d.q)
     stream = torch.cuda.current_stream()
 
+    host = np.ascontiguousarray(w.qo_indptr, dtype=np.int32)
+
     def call():
         binding.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale, window=window,
-                        page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out)
+                        page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out,
+                        qo_indptr_host=host)
 
     for _ in range(warmup):
         call()

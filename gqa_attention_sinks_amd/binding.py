@@ -68,7 +68,7 @@ def load_library():
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.sinkattn_prefill.argtypes = [vp, vp, ctypes.POINTER(_KV), vp, vp, vp, i32, i32, i32, i32, i32,
-                                     f32, i32, vp]
+                                     f32, i32, vp, vp]
     lib.sinkattn_prefill.restype = i32
     lib.sinkattn_decode_paged.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp, i32, i32,
                                           i32, i32, f32, i32, vp]
@@ -158,13 +158,15 @@ def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
 
 def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int = 0,
             page_indices=None, kv_len=None, out=None, lse=None, return_lse: bool = False,
-            stream=None):
+            qo_indptr_host=None, stream=None):
     """Causal / sliding-window prefill (``sinkattn_prefill``).
 
     ``q`` [total_q, Hq, 64] bf16; ``qo_indptr`` [B+1] int32.  Contiguous KV:
     ``k``/``v`` [total_kv, Hkv, 64] with ``kv_indptr`` row offsets.  Paged KV:
     ``k``/``v`` [num_pages, Hkv, 16, 64] with ``kv_indptr`` page offsets,
     ``page_indices`` and ``kv_len``.  ``sinks`` [Hq] fp32 or None.
+    ``qo_indptr_host``: optional host copy of ``qo_indptr`` (numpy/list) that
+    lets the library size the launch exactly.
     Returns ``out`` (and ``lse`` [total_q, Hq] fp32 when asked).
     """
     torch = _torch()
@@ -185,10 +187,17 @@ def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int =
         lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _dev(lse, "lse", torch.float32, (total_q, hq))
+    host = None
+    if qo_indptr_host is not None:
+        host = np.ascontiguousarray(qo_indptr_host, dtype=np.int32)
+        if host.shape != (batch + 1,):
+            raise ValueError("qo_indptr_host must have batch + 1 entries")
     lib = load_library()
     _check(lib.sinkattn_prefill(_ptr(q), _ptr(qo_indptr), ctypes.byref(kvs), _ptr(sinks), _ptr(out),
                                 _ptr(lse), batch, total_q, hq, hkv, HEAD_DIM, float(sm_scale),
-                                int(window), _stream(stream)))
+                                int(window),
+                                None if host is None else host.ctypes.data_as(ctypes.c_void_p),
+                                _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -75,7 +75,8 @@ extern "C" {
 sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const sinkattn_kv* kv,
                                  const float* sinks, void* out, float* lse, int32_t batch,
                                  int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, float sm_scale, int32_t window, void* stream) {
+                                 int32_t head_dim, float sm_scale, int32_t window,
+                                 const int32_t* qo_indptr_host, void* stream) {
   REQUIRE(q != nullptr && qo_indptr != nullptr && out != nullptr, SINKATTN_ERR_INVALID_ARG,
           "q, qo_indptr and out are required");
   sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
@@ -105,13 +106,30 @@ sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const 
   a.paged = kv->paged;
   // single-row requests (decode rows of a mixed batch) go to the decode kernel when paged
   a.skip_single_rows = kv->paged;
-  const long slots = (long)total_q / bm + batch;   // >= sum over requests of ceil(n_q / bm)
+  long slots = (long)total_q / bm + batch;   // >= sum over requests of ceil(n_q / bm)
+  bool any_single = true;                    // a request with one row may exist
+  if (qo_indptr_host != nullptr) {           // exact plan from the host copy
+    slots = 0;
+    any_single = false;
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t n = (int64_t)qo_indptr_host[b + 1] - qo_indptr_host[b];
+      REQUIRE(n >= 1, SINKATTN_ERR_INVALID_ARG, "request %d has no query row", b);
+      if (kv->paged && n == 1) {
+        any_single = true;
+        continue;
+      }
+      slots += (n + bm - 1) / bm;
+    }
+    REQUIRE(qo_indptr_host[batch] == total_q, SINKATTN_ERR_INVALID_ARG,
+            "qo_indptr_host[batch] (%d) != total_q (%d)", qo_indptr_host[batch], total_q);
+  }
   REQUIRE(slots * num_qo_heads < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
   a.num_slots = (int32_t)slots;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(sinkattn::launch_prefill(a, total_q, s), "prefill launch")) != SINKATTN_OK) return st;
-  if (kv->paged) {
+  if (slots > 0 && (st = hip_status(sinkattn::launch_prefill(a, total_q, s), "prefill launch")) != SINKATTN_OK)
+    return st;
+  if (kv->paged && any_single) {
     sinkattn::DecodeArgs d{};
     d.q = a.q;
     d.k_pool = a.k;

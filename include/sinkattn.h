@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 1
+#define SINKATTN_ABI_VERSION 2
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
@@ -103,13 +103,22 @@ typedef struct sinkattn_kv {
  *   sinks      [Hq] fp32 or NULL (no sink)
  *   out        [total_q, Hq, 64] bf16, written
  *   lse        [total_q, Hq] fp32 natural-log LSE (sink included), or NULL
- *   total_q    number of query rows (= qo_indptr[batch]); sizes the launch
+ *   total_q    number of query rows (= qo_indptr[batch]); bounds the launch
  *   window     0 = full causal, W > 0 = each row sees its last W positions
- *              (its own included) */
+ *              (its own included)
+ *   qo_indptr_host  optional host copy of qo_indptr ([batch+1], host memory,
+ *              read during the call only).  The CPU-side plan of the launch
+ *              ("Accelerating Sonar through speculation", section "Inference
+ *              with speculative decoding": the CPU fills the buffers that
+ *              configure and schedule the attention kernel): with it the
+ *              prefill grid holds exactly the query tiles of the batch;
+ *              without it the grid is sized from total_q and batch and the
+ *              surplus workgroups exit at once.  Results are identical. */
 sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const sinkattn_kv* kv,
                                  const float* sinks, void* out, float* lse, int32_t batch,
                                  int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,
-                                 int32_t head_dim, float sm_scale, int32_t window, void* stream);
+                                 int32_t head_dim, float sm_scale, int32_t window,
+                                 const int32_t* qo_indptr_host, void* stream);
 
 /* One query token per request over a paged KV cache, split along the KV
  * sequence into num_splits chunks of whole pages: with n_pages =

@@ -64,12 +64,12 @@ class DeviceWorkload:
         self.page_indices = i32_to_dev(w.page_indices) if w.paged else None
         self.sinks = f32_to_dev(w.sinks)
 
-    def prefill(self, window, sinks=True, return_lse=True):
+    def prefill(self, window, sinks=True, return_lse=True, host_plan=True):
         w = self.w
         return sa.prefill(self.q, self.qo_indptr, self.k, self.v, self.kv_indptr,
                           self.sinks if sinks else None, w.scale, window=window,
                           page_indices=self.page_indices, kv_len=self.kv_len if w.paged else None,
-                          return_lse=return_lse)
+                          return_lse=return_lse, qo_indptr_host=w.qo_indptr if host_plan else None)
 
     def decode(self, num_splits, window=0, merge=True, return_lse=True):
         w = self.w

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 1
+    assert sa.abi_version() == 2
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -85,9 +85,11 @@ def _kv(paged=1, page_size=16, k=FAKE, page_indices=FAKE, kv_len=FAKE):
                        kv_len if paged else None)
 
 
-def _prefill(lib, kv, q=FAKE, qo=FAKE, out=FAKE, batch=2, total_q=4, hq=8, hkv=2, d=64, scale=0.125, window=0):
+def _prefill(lib, kv, q=FAKE, qo=FAKE, out=FAKE, batch=2, total_q=4, hq=8, hkv=2, d=64, scale=0.125, window=0,
+             host=None):
+    hp = None if host is None else np.ascontiguousarray(host, dtype=np.int32).ctypes.data_as(ctypes.c_void_p)
     return lib.sinkattn_prefill(q, qo, ctypes.byref(kv) if kv is not None else None, None, out, None,
-                                batch, total_q, hq, hkv, d, ctypes.c_float(scale), window, None)
+                                batch, total_q, hq, hkv, d, ctypes.c_float(scale), window, hp, None)
 
 
 def _decode(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, hq=8, hkv=2, d=64, scale=0.125,
@@ -111,6 +113,13 @@ def _decode(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, hq=8, h
 def test_prefill_argument_errors(lib, kwargs, code):
     assert _prefill(lib, _kv(), **kwargs) == code
     assert lib.sinkattn_last_error()
+
+
+def test_prefill_host_plan_errors(lib):
+    # the host copy of qo_indptr must agree with total_q and give every request a row
+    assert _prefill(lib, _kv(), host=[0, 2, 3]) == INVALID
+    assert _prefill(lib, _kv(), host=[0, 0, 4]) == INVALID
+    assert _prefill(lib, _kv(), host=[0, 4, 4]) == INVALID
 
 
 def test_prefill_kv_errors(lib):

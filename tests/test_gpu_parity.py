@@ -61,6 +61,24 @@ def test_prefill_ragged_small(window, paged):
     assert_parity(to_host(out), ro, f"prefill ragged w={window} paged={paged}", to_host(lse), rl)
 
 
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_host_plan_is_invisible(paged):
+    """The exact launch from the host copy of qo_indptr and the upper-bound
+    launch without it give bitwise identical results."""
+    rng = np.random.default_rng(21)
+    kv_len = np.array([300, 1, 77, 513, 2])
+    qo_len = np.array([300, 1, 20, 257, 1])
+    maker = wl.make_paged if paged else wl.make_contiguous
+    w = maker("plan", kv_len, qo_len, 16, 2, rng=rng)
+    say(f"prefill host plan paged={paged}")
+    d = DeviceWorkload(w)
+    for window in [0, 128]:
+        a_out, a_lse = d.prefill(window=window, host_plan=True)
+        b_out, b_lse = d.prefill(window=window, host_plan=False)
+        assert np.array_equal(to_host(a_out), to_host(b_out))
+        assert np.array_equal(to_host(a_lse), to_host(b_lse))
+
+
 @pytest.mark.parametrize("group", [1, 4, 16])
 def test_prefill_group_sizes_and_no_sinks(group):
     rng = np.random.default_rng(12 + group)

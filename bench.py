@@ -52,8 +52,10 @@ def parse():
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="paged_decode",
-                   choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill"],
-                   help="for profiling runs: time only this workload")
+                   choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
+                            "copy_calibration"],
+                   help="for profiling runs: time only this workload (copy_calibration: a plain "
+                        "256 MiB device copy, the reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -131,23 +133,15 @@ def time_decode(w, args, torch, dev):
     opart, lpart, lsep = P(o_part.data_ptr()), P(lse_part.data_ptr()), P(lse.data_ptr())
     scale = ctypes.c_float(w.scale)
 
-    def step(i, ev=None):
+    def step(i):
         r = i % len(reps)
-        if ev is not None:
-            ev[0].record(stream)
         if s > 1:
             st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
                                            B, H, HKV, 64, scale, 0, sp)
-            if ev is not None:
-                ev[1].record(stream)
             st |= lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lsep, sp)
         else:
             st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lsep,
                                            B, H, HKV, 64, scale, 0, sp)
-            if ev is not None:
-                ev[1].record(stream)
-        if ev is not None:
-            ev[2].record(stream)
         if st != 0:
             raise RuntimeError(lib.sinkattn_last_error().decode())
 
@@ -161,13 +155,28 @@ def time_decode(w, args, torch, dev):
     wall = (time.perf_counter() - t0) / args.steps
     last = (args.steps - 1) % len(reps)
     out_host = outs[last].float().cpu().numpy().astype(np.float64)
-    # per-kernel durations with events on the launch stream (separate pass)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the decode kernel alone: K back-to-back launches between two events on
+    # the stream they run on (rotating the replicas), then the merge alone
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        r = i % len(reps)
+        if s > 1:
+            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
+                                           B, H, HKV, 64, scale, 0, sp)
+        else:
+            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lsep,
+                                           B, H, HKV, 64, scale, 0, sp)
+        if st != 0:
+            raise RuntimeError(lib.sinkattn_last_error().decode())
+    e1.record(stream)
+    if s > 1:
+        for i in range(args.steps):
+            lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[i % len(reps)], lsep, sp)
+    e2.record(stream)
     torch.cuda.synchronize()
-    dec_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    mer_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    dec_ms = e0.elapsed_time(e1) / args.steps
+    mer_ms = e1.elapsed_time(e2) / args.steps if s > 1 else 0.0
     return dict(step_ms=wall * 1e3, decode_ms=dec_ms, merge_ms=mer_ms, splits=s, out=out_host)
 
 
@@ -196,6 +205,23 @@ def time_prefill(w, steps, warmup, torch, dev, window=0):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps
     return dict(step_ms=wall * 1e3, kernel_ms=e0.elapsed_time(e1) / steps, out=out)
+
+
+def measured_traffic(kernel, workload, splits):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE runs, or
+    None when the kernel's sources changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in ("decode.hip", "device_common.hpp", "kernel_args.hpp")]
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
+    if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
+            or rec.get("num_splits") != splits:
+        return None
+    return int(round(rec["bytes"]))
 
 
 def parity(g, r):
@@ -276,7 +302,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic("decode_paged_kernel", "paged_decode", res["splits"]),
             "kernel": "decode_paged_kernel",
         },
     }
@@ -308,6 +334,19 @@ def main():
 
 def profile_only(args, torch, dev, wl):
     """Time one named workload only (for rocprofv3 runs)."""
+    if args.workload == "copy_calibration":
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
+                          "ms": dt * 1e3, "GBs_rw": 2 * n / dt / 1e9}))
+        return
     w = getattr(wl, args.workload)()
     log(f"timing {args.workload}")
     if args.workload == "long_split_decode":

@@ -254,20 +254,30 @@ void prefill_kernel(PrefillArgs a) {
       uint8_t* vs = ks + kTileBytes;
       // S^T = K . Q^T : [key block][row block]
       f32x16 s[2][2];
+      // all eight K operands are read before the first MFMA, so the LDS
+      // latency is paid once per tile rather than once per MFMA pair
+      bf16x8 kop[2][4];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int kstep = 0; kstep < 4; ++kstep)
+          kop[kb][kstep] = *reinterpret_cast<const bf16x8*>(ks + tile_swizzle(32 * kb + r32, 2 * kstep + half));
       mfma_phase_begin();
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb][0] = f32x16{};
         s[kb][1] = f32x16{};
-        const int key = 32 * kb + r32;
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
-          const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + tile_swizzle(key, 2 * kstep + half));
-          s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[0][kstep], s[kb][0], 0, 0, 0);
-          s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, qop[1][kstep], s[kb][1], 0, 0, 0);
+          s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][kstep], qop[0][kstep], s[kb][0], 0, 0, 0);
+          s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][kstep], qop[1][kstep], s[kb][1], 0, 0, 0);
         }
       }
       mfma_phase_end();
+#if SINKATTN_PREFILL_SCHED
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the eight K reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the sixteen MFMAs
+#endif
       // causal diagonal / window edge: element i of key block kb is key
       // kt + 32*kb + 8*(i/4) + 4*half + i%4
       const bool need_mask = (kt + kBN - 1 > wp_min) || (W > 0 && kt < wp_max - W + 1);
@@ -318,6 +328,23 @@ void prefill_kernel(PrefillArgs a) {
             for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
         }
       }
+      // V^T operands for the P.V product, read from LDS before the weights
+      // are computed so their latency hides behind the vector work
+      f16x8 vtop[4][2];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int key_a = 16 * r + 4 * half + (j16 >> 2);
+        const int key_b = key_a + 8;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int chunk = 4 * db + 2 * gr_odd + ((j16 & 3) >> 1);
+          const int sub = 8 * (j16 & 1);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_a, chunk) + sub));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_b, chunk) + sub));
+          typedef __attribute__((ext_vector_type(8))) short i16x8;
+          vtop[r][db] = __builtin_bit_cast(f16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        }
+      }
       // P^T operands (fp16): operand r covers keys 16r .. 16r+15 of the tile
       f16x8 pop[2][4];
 #pragma unroll
@@ -340,24 +367,15 @@ void prefill_kernel(PrefillArgs a) {
             pop[rb][2 * kb + hh] = __builtin_bit_cast(f16x8, pk);
           }
       }
-      // O^T += V^T . P^T ; V^T operands from transposed LDS reads, shared by both row blocks
+      // O^T += V^T . P^T ; each V^T operand feeds both row blocks
       mfma_phase_begin();
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key_a = 16 * r + 4 * half + (j16 >> 2);
-        const int key_b = key_a + 8;
+      for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const int chunk = 4 * db + 2 * gr_odd + ((j16 & 3) >> 1);
-          const int sub = 8 * (j16 & 1);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_a, chunk) + sub));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_b, chunk) + sub));
-          typedef __attribute__((ext_vector_type(8))) short i16x8;
-          const f16x8 vt = __builtin_bit_cast(f16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-          acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pop[0][r], acc[0][db], 0, 0, 0);
-          acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt, pop[1][r], acc[1][db], 0, 0, 0);
+          acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vtop[r][db], pop[0][r], acc[0][db], 0, 0, 0);
+          acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vtop[r][db], pop[1][r], acc[1][db], 0, 0, 0);
         }
-      }
       mfma_phase_end();
     }
 

@@ -13,7 +13,7 @@
 #include "sinkattn.h"
 
 namespace sinkattn {
-int prefill_rows_per_tile();
+int prefill_rows_per_tile(int32_t window);
 }
 
 namespace {
@@ -85,7 +85,7 @@ sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const 
   REQUIRE(total_q >= batch, SINKATTN_ERR_INVALID_ARG, "total_q (%d) must be >= batch (%d): every request has a query row",
           total_q, batch);
 
-  const int bm = sinkattn::prefill_rows_per_tile();
+  const int bm = sinkattn::prefill_rows_per_tile(window);
   sinkattn::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.qo_indptr = qo_indptr;

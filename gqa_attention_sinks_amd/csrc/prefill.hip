@@ -8,24 +8,31 @@
 // Work decomposition (gfx950):
 //   workgroup = (tile of 256 query rows of one request, one query head);
 //   4 waves x 64 query rows (two 32-row MFMA blocks, so every K/V operand
-//   read from LDS feeds two MFMAs).  Consecutive workgroup ids walk the KV heads
-//   first, so with 8 KV heads and 8 XCDs each XCD's L2 serves one KV head.
-//   Tiles of a request are issued longest first (causal work grows with the
-//   row index).
+//   read from LDS feeds two MFMAs); two workgroups per CU, so each SIMD runs
+//   two waves whose matrix and vector phases overlap.  Consecutive workgroup
+//   ids walk the KV heads first, so with 8 KV heads and 8 XCDs each XCD's L2
+//   serves one KV head.  Tiles of a request are issued longest first (causal
+//   work grows with the row index).
 //   Per KV tile of 64 keys (K and V staged in LDS, double buffered, 16-byte
-//   chunks XOR-swizzled by key):
+//   chunks swizzled so that every LDS access pattern below is free of bank
+//   conflicts):
 //     S^T[64 keys x 64 rows] = K . Q^T    -> 16 x MFMA 32x32x16 bf16 (Q^T in registers)
 //     base-2 online softmax on the accumulator: each lane holds two query
-//     rows and 32 of their keys, so a row max needs one exchange with
-//     lane ^ 32; the reference max moves lazily (only when a row max exceeds
-//     it by 2^8), so most tiles skip rescaling the accumulators
+//     rows and 32 of their keys
 //     O^T[64 dims x 64 rows] += V^T . P^T -> 16 x MFMA 32x32x16 fp16
 //       (P^T is the score accumulator converted to fp16; V is converted to
 //        fp16 once when its tile is staged, and V^T comes from the natural
 //        [key][dim] LDS tile through ds_read_b64_tr_b16).  fp16 weights carry
-//        three more mantissa bits than bf16; they are taken relative to the
-//        running key maximum and the sink is folded in at the end, which
-//        gives exactly the state of the sink-seeded recurrence.
+//        three more mantissa bits than bf16; they are taken relative to a
+//        reference at or below the running key maximum, and the sink is
+//        folded in at the end, which gives exactly the state of the
+//        sink-seeded recurrence.
+//   The reference moves only when it must: a tile's weights are first taken
+//   against the current reference, and only if some lane's share of a row's
+//   weight sum exceeds 2^14 (a key far above the reference; fp16 weights stay
+//   finite below 65504) does the wave find the tile's row maxima, move the
+//   reference up, rescale and recompute.  A row's first tile always does (the
+//   reference starts at -FLT_MAX), later ones almost never.
 //   Masking is applied only on tiles that cross the causal diagonal or the
 //   window's lower edge.
 
@@ -39,30 +46,23 @@ constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 64;               // two 32-row MFMA blocks per wave
 constexpr int kBM = kWaves * kRowsPerWave;     // query rows per workgroup
 constexpr int kBN = 64;                        // keys per tile
-constexpr float kLazy = 8.f;                   // log2 slack before the running max moves
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 8 KiB
+constexpr float kSumLimit = 16384.f;           // 2^14
+constexpr float kFloatMax = 3.402823466e38f;
 
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-
-__device__ __forceinline__ int tile_swizzle(int key, int chunk) {
-  return key * 128 + ((chunk ^ (key & 7)) << 4);
+// Byte offset of 16-byte chunk `chunk` of key row `key` in a staged tile
+// ([key][64 dims], 128 bytes a row).  The chunk position is XORed with a
+// function of key bits 1-3 chosen so that the three access patterns of the
+// kernel are conflict-free on the 64 four-byte LDS banks: the K operand reads
+// (16 lanes per cycle on 16 consecutive keys), the transposing V reads (32
+// lanes per cycle on 4 consecutive keys x 4 chunks) and the staging stores.
+__device__ __forceinline__ uint32_t tile_swizzle(int key, int chunk) {
+  const int a = (key >> 1) & 7;
+  return key * 128 + ((chunk ^ (a ^ ((a & 1) << 2))) << 4);
 }
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
-}
-
-// Wave priority around MFMA clusters: while one wave of a SIMD issues its
-// matrix instructions, the other wave's vector instructions fill the gaps.
-__device__ __forceinline__ void mfma_phase_begin() {
-#if SINKATTN_PREFILL_SETPRIO
-  __builtin_amdgcn_s_setprio(1);
-#endif
-}
-__device__ __forceinline__ void mfma_phase_end() {
-#if SINKATTN_PREFILL_SETPRIO
-  __builtin_amdgcn_s_setprio(0);
-#endif
 }
 
 template <typename T>
@@ -70,11 +70,58 @@ __device__ __forceinline__ __attribute__((address_space(3))) T* lds_ptr(uint8_t*
   return (__attribute__((address_space(3))) T*)(p);
 }
 
+// LDS pointer from a byte address in the workgroup's LDS (no null check).
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(3))) T* lds_at(uint32_t addr) {
+  return (__attribute__((address_space(3))) T*)(size_t)addr;
+}
+
+// A per-tile LDS base (stage address + lane offset) that the compiler may not
+// re-associate with the constant part of each read: otherwise it hoists one
+// precomputed address per read out of the loop (a register and two adds each).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  __asm__ volatile("" : "+v"(x));
+  return x;
+}
+
+// Scheduling hints: issue a block's `reads` LDS reads before its first MFMA,
+// so that their latencies overlap instead of each read waiting for the MFMAs
+// before it (which is what the register-pressure-driven default does).
+template <int READS, int MFMAS>
+__device__ __forceinline__ void reads_then_mfmas() {
+  __builtin_amdgcn_sched_group_barrier(0x100, READS, 0);
+  __builtin_amdgcn_sched_group_barrier(0x008, MFMAS, 0);
+}
+
+// Per-lane byte offsets inside one staged tile, computed once; the key-block
+// parts of each read (+32 keys, +16 keys) are constants in the offset field.
+struct TileLanes {
+  uint32_t k[4];      // K operand of MFMA step kstep: key r32, chunk 2*kstep + half
+  uint32_t v[2][2];   // V^T operand, dims block db, keys kq (lo) and kq + 8 (hi)
+};
+
+__device__ __forceinline__ TileLanes tile_lanes(int lane) {
+  TileLanes t;
+  const int r32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int kstep = 0; kstep < 4; ++kstep) t.k[kstep] = tile_swizzle(r32, 2 * kstep + half);
+  const int j16 = lane & 15;
+  const int kq = 4 * half + (j16 >> 2);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    const int chunk = 4 * db + 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+    t.v[db][0] = tile_swizzle(kq, chunk) + 8 * (j16 & 1);
+    t.v[db][1] = tile_swizzle(kq + 8, chunk) + 8 * (j16 & 1);
+  }
+  return t;
+}
+
 // Find the (request, tile) handled by tile slot `slot`: tiles are numbered
 // request by request; every thread sums a run of requests, then a block scan.
 __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* out_b, int* out_tile) {
+  constexpr int kThreads = kWaves * 64;
   const int tid = threadIdx.x;
-  const int per = (a.batch + kWaves * 64 - 1) / (kWaves * 64);
+  const int per = (a.batch + kThreads - 1) / kThreads;
   const int b0 = min(tid * per, a.batch);
   const int b1 = min(b0 + per, a.batch);
   int local = 0;
@@ -84,7 +131,7 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   }
   s_scan[tid] = local;
   __syncthreads();
-  for (int off = 1; off < kWaves * 64; off <<= 1) {
+  for (int off = 1; off < kThreads; off <<= 1) {
     const int v = tid >= off ? s_scan[tid - off] : 0;
     __syncthreads();
     s_scan[tid] += v;
@@ -113,6 +160,34 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   return s_found[0] >= 0;
 }
 
+// fp16 weights of one 32-key half of a tile against the reference m (base 2),
+// packed as P^T operands (pop[rb][hh] covers keys 16*hh .. 16*hh+15 of the
+// half, in the key order of the score accumulator), and this lane's share of
+// each row's weight sum.  The sum is taken over the fp32 weights with plain
+// adds: the packed fp16 dot instruction would occupy the matrix pipe.
+__device__ __forceinline__ void half_weights(const f32x16 (&s)[2], const float (&m)[2], float c,
+                                             f16x8 (&pop)[2][2], float (&tsum)[2]) {
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    float part[2] = {0.f, 0.f};
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      float pv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pv[e] = exp2_hw(__builtin_fmaf(s[rb][8 * hh + e], c, -m[rb]));
+      u32x4 pk;
+      pk[0] = pack_f16x2(pv[0], pv[1]);
+      pk[1] = pack_f16x2(pv[2], pv[3]);
+      pk[2] = pack_f16x2(pv[4], pv[5]);
+      pk[3] = pack_f16x2(pv[6], pv[7]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[e & 1] += pv[e];
+      pop[rb][hh] = __builtin_bit_cast(f16x8, pk);
+    }
+    tsum[rb] = part[0] + part[1];
+  }
+}
+
 template <bool PAGED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
@@ -133,7 +208,7 @@ void prefill_kernel(PrefillArgs a) {
   const int head = g * a.group + hg;
 
   int b, tile;
-  if (!locate_tile(a, slot, s_scan, &b, &tile)) return;
+  if (!locate_tile(a, slot, s_scan, &b, &tile)) return;   // uniform over the workgroup
   b = __builtin_amdgcn_readfirstlane(b);
   tile = __builtin_amdgcn_readfirstlane(tile);
 
@@ -174,44 +249,53 @@ void prefill_kernel(PrefillArgs a) {
       qop[rb][ks] = ok ? __builtin_bit_cast(bf16x8, ldg16(qp + 16 * ks)) : bf16x8{};
   }
 
-  // Key-domain streaming state per row: running max reference m (base 2; may
-  // lag the true key maximum by up to kLazy), this lane's part of the
-  // denominator, and the P.V accumulator.  The sink is folded in at the end
-  // (fold_sink), which yields the state of the sink-seeded recurrence.
-  float m[2] = {kNegInf, kNegInf}, dsum[2] = {0.f, 0.f};
+  // Key-domain streaming state per row: reference m (base 2; at or below the
+  // key maximum seen), this lane's part of the denominator, and the P.V
+  // accumulator.  The sink is folded in at the end (fold_sink), which yields
+  // the state of the sink-seeded recurrence.
+  float m[2] = {-kFloatMax, -kFloatMax}, dsum[2] = {0.f, 0.f};
   f32x16 acc[2][2] = {};   // [row block][dim block]
   const float c = a.scale_log2;
+  const TileLanes tl = tile_lanes(lane);
+  const uint32_t smem0 = (uint32_t)(size_t)lds_ptr<uint8_t>(smem);   // LDS byte address
 
-  // tile loader: thread -> (key = tid / 4, 32 bytes at dims 16 * (tid % 4))
+  // Staging: thread -> key tid/4, 32 bytes at dims 16*(tid%4) of K and of V.
+  // A wave's sixteen keys are consecutive and share a page, so the address is
+  // a uniform base (scalar registers) plus a fixed per-lane offset.  Keys past
+  // the last one re-read the last key and are zeroed when staged, so the
+  // common full tile carries no per-row checks.
   const int ld_key = tid >> 2;
   const int ld_c = (tid & 3) * 2;   // first 16-byte chunk
-  const size_t g_off = (size_t)g * (PAGED ? kPageSize * kHeadDim : kHeadDim) + ld_c * 8;
+  const int wkey = 16 * wave;       // first key of this wave's rows
+  const int lkey = lane >> 2;       // this lane's key among them
   const int32_t* page_list = PAGED ? a.page_indices + a.kv_indptr[b] : nullptr;
-  // paged: id of the page holding this thread's key, fetched one tile ahead
+  const uint32_t key_bytes = PAGED ? kHeadDim * 2 : (uint32_t)a.num_kv_heads * kHeadDim * 2;
+  const uint32_t lane_off_full = (uint32_t)lkey * key_bytes + ld_c * 16;
+  const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k);
+  const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(a.v);
+  // paged: the page holding the wave's first (clamped) key, fetched a tile ahead
   auto page_of = [&](int kt) -> int {
-    return page_list[min(kt + ld_key, n_k - 1) / kPageSize];
+    return page_list[min(kt + wkey, n_k - 1) / kPageSize];
   };
-  int pid = 0;
-  auto load_rows = [&](int key, int page, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
-    size_t row;
-    if (PAGED) row = ((size_t)page * a.num_kv_heads * kPageSize + key % kPageSize) * kHeadDim + g_off;
-    else row = (size_t)(kv_begin + key) * a.num_kv_heads * kHeadDim + g_off;
-    const uint16_t* kp = a.k + row;
-    const uint16_t* vp = a.v + row;
-    kr[0] = ldg16(kp);
-    kr[1] = ldg16(kp + 8);
-    vr[0] = ldg16(vp);
-    vr[1] = ldg16(vp + 8);
-  };
-  // rows past the last key read the last key's row (always in bounds) and are
-  // zeroed when staged, so the common full tile carries no per-row checks
   auto load_tile = [&](int kt, int page, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
-    load_rows(min(kt + ld_key, n_k - 1), page, kr, vr);
+    const int k0 = min(kt + wkey, n_k - 1);
+    const size_t base = PAGED ? ((size_t)page * a.num_kv_heads + g) * (kPageSize * kHeadDim * 2)
+                              : ((size_t)(kv_begin + k0) * a.num_kv_heads + g) * (kHeadDim * 2);
+    uint32_t off = lane_off_full;
+    if (kt + kBN > n_k) {            // uniform: only the range's last tile
+      __asm__ volatile("");
+      const int key = min(kt + wkey + lkey, n_k - 1);
+      off = (uint32_t)(PAGED ? key % kPageSize : key - k0) * key_bytes + ld_c * 16;
+    }
+    kr[0] = *reinterpret_cast<const u32x4*>(kbytes + base + off);
+    kr[1] = *reinterpret_cast<const u32x4*>(kbytes + base + off + 16);
+    vr[0] = *reinterpret_cast<const u32x4*>(vbytes + base + off);
+    vr[1] = *reinterpret_cast<const u32x4*>(vbytes + base + off + 16);
   };
   auto store_tile = [&](int stage, int kt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
     uint8_t* ks = smem + stage * 2 * kTileBytes;
     uint8_t* vs = ks + kTileBytes;
-    if (kt + kBN > n_k) {           // uniform: only the last tile of the range
+    if (kt + kBN > n_k) {            // uniform: only the range's last tile
       __asm__ volatile("");
       if (kt + ld_key >= n_k) kr[0] = kr[1] = vr[0] = vr[1] = u32x4{};
     }
@@ -227,6 +311,7 @@ void prefill_kernel(PrefillArgs a) {
     *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c + 1)) = v16[1];
   };
 
+  int pid = 0;
   {
     u32x4 kr[2], vr[2];
     if (PAGED) pid = page_of(k_first);
@@ -235,9 +320,6 @@ void prefill_kernel(PrefillArgs a) {
     store_tile(0, k_first, kr, vr);
   }
   __syncthreads();
-
-  const int j16 = lane & 15;
-  const int gr_odd = (lane >> 4) & 1;
 
   for (int it = 0; it < ntiles; ++it) {
     const int kt = k_first + it * kBN;
@@ -250,76 +332,85 @@ void prefill_kernel(PrefillArgs a) {
 
     const bool wave_skip = !wave_live || kt > wp_max || (W > 0 && kt + kBN - 1 < wp_min - W + 1);
     if (!wave_skip) {
-      uint8_t* ks = smem + (it & 1) * 2 * kTileBytes;
-      uint8_t* vs = ks + kTileBytes;
-      // S^T = K . Q^T : [key block][row block]
-      f32x16 s[2][2];
-      // all eight K operands are read before the first MFMA, so the LDS
-      // latency is paid once per tile rather than once per MFMA pair
-      bf16x8 kop[2][4];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      const uint32_t st = smem0 + (it & 1) * 2 * kTileBytes;
+      const bool need_mask = (kt + kBN - 1 > wp_min) || (W > 0 && kt < wp_max - W + 1);
+      // The tile is processed as two 32-key halves, pipelined inside the
+      // wave so that matrix and vector instructions stay independent and can
+      // issue side by side:
+      //   S0 | S1 with weights(S0) | P0.V0 with weights(S1) | P1.V1
+      // Element i of s[rb] (half kb) is key kt + 32*kb + 8*(i/4) + 4*half + i%4
+      // against row r32 + 32*rb.
+      auto read_k = [&](int kb, bf16x8 (&kop)[4]) {
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep)
-          kop[kb][kstep] = *reinterpret_cast<const bf16x8*>(ks + tile_swizzle(32 * kb + r32, 2 * kstep + half));
-      mfma_phase_begin();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb][0] = f32x16{};
-        s[kb][1] = f32x16{};
+          kop[kstep] = *lds_at<const bf16x8>(opaque(st + tl.k[kstep]) + kb * 32 * 128);
+      };
+      auto mma_scores = [&](const bf16x8 (&kop)[4], f32x16 (&sh)[2]) {
+        sh[0] = f32x16{};
+        sh[1] = f32x16{};
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep) {
-          s[kb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][kstep], qop[0][kstep], s[kb][0], 0, 0, 0);
-          s[kb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kb][kstep], qop[1][kstep], s[kb][1], 0, 0, 0);
+          sh[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kstep], qop[0][kstep], sh[0], 0, 0, 0);
+          sh[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kstep], qop[1][kstep], sh[1], 0, 0, 0);
         }
-      }
-      mfma_phase_end();
-#if SINKATTN_PREFILL_SCHED
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);   // the eight K reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // then the sixteen MFMAs
-#endif
-      // causal diagonal / window edge: element i of key block kb is key
-      // kt + 32*kb + 8*(i/4) + 4*half + i%4
-      const bool need_mask = (kt + kBN - 1 > wp_min) || (W > 0 && kt < wp_max - W + 1);
-      if (need_mask) {
+      };
+      auto mask_half = [&](int kb, f32x16 (&sh)[2]) {
         // a real (scalar) branch: only tiles on the diagonal or the window edge pay for it
         __asm__ volatile("");
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const int hi_off = my_p[rb] - kt - 4 * half;
-          const int lo_off = W > 0 ? my_lo[rb] - kt - 4 * half : -kBN;
+          const int hi_off = my_p[rb] - kt - 32 * kb - 4 * half;
+          const int lo_off = W > 0 ? my_lo[rb] - kt - 32 * kb - 4 * half : -kBN;
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int off = 32 * kb + 8 * (i >> 2) + (i & 3);
-              s[kb][rb][i] = (off <= hi_off && off >= lo_off) ? s[kb][rb][i] : kNegInf;
-            }
+          for (int i = 0; i < 16; ++i) {
+            const int off = 8 * (i >> 2) + (i & 3);
+            sh[rb][i] = (off <= hi_off && off >= lo_off) ? sh[rb][i] : kNegInf;
+          }
         }
-      }
-      // row maxima; the reference max moves only when a row's max exceeds it
-      // by more than kLazy (weights stay <= 2^kLazy), so most tiles skip the
-      // rescale of the accumulators
-      float cand[2];
-      bool grow = false;
+      };
+      auto read_v = [&](int kb, f16x8 (&vt)[2][2]) {   // [hh][db]
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        // a running chain compiles to one v_max3 per two values
-        float mx = s[0][rb][0];
+        for (int db = 0; db < 2; ++db) {
+          const uint32_t vlo = opaque(st + kTileBytes + tl.v[db][0]);
+          const uint32_t vhi = opaque(st + kTileBytes + tl.v[db][1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][rb][i]);
+          for (int hh = 0; hh < 2; ++hh) {
+            const int r = 2 * kb + hh;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<i16x4>(vlo + r * 16 * 128));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_at<i16x4>(vhi + r * 16 * 128));
+            typedef __attribute__((ext_vector_type(8))) short i16x8;
+            vt[hh][db] = __builtin_bit_cast(f16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          }
+        }
+      };
+      auto mma_pv = [&](const f16x8 (&vt)[2][2], const f16x8 (&pop)[2][2]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][rb][i]);
-        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-        cand[rb] = mx * c;
-        grow |= cand[rb] > m[rb] + kLazy;
-      }
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) {
+            acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[hh][db], pop[0][hh], acc[0][db], 0, 0, 0);
+            acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[hh][db], pop[1][hh], acc[1][db], 0, 0, 0);
+          }
+      };
+      // rare path of a half (always on a row's first tile): recompute its
+      // scores from the staged tile, move the reference to the row maxima,
+      // rescale, and redo the weights
+      auto rebase = [&](int kb, f16x8 (&pop)[2][2], float (&tsum)[2]) {
         __asm__ volatile("");
+        bf16x8 kop[4];
+        read_k(kb, kop);
+        f32x16 sh[2];
+        mma_scores(kop, sh);
+        reads_then_mfmas<4, 8>();
+        if (need_mask) mask_half(kb, sh);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-          const float m_new = cand[rb] > m[rb] + kLazy ? cand[rb] : m[rb];
-          const float alpha = (m_new == m[rb]) ? 1.f : exp2_hw(m[rb] - m_new);
+          float mx = sh[rb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, sh[rb][i]);
+          mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+          const float m_new = fmaxf(m[rb], mx * c);
+          const float alpha = exp2_hw(m[rb] - m_new);
           m[rb] = m_new;
           dsum[rb] *= alpha;
 #pragma unroll
@@ -327,56 +418,60 @@ void prefill_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[rb][db][i] *= alpha;
         }
+        half_weights(sh, m, c, pop, tsum);
+      };
+
+      f32x16 s0[2], s1[2];
+      f16x8 p0[2][2], p1[2][2];
+      float t0s[2], t1s[2];
+      {
+        bf16x8 kop[4];
+        read_k(0, kop);
+        mma_scores(kop, s0);
+        reads_then_mfmas<4, 8>();
       }
-      // V^T operands for the P.V product, read from LDS before the weights
-      // are computed so their latency hides behind the vector work
-      f16x8 vtop[4][2];
+      if (need_mask) mask_half(0, s0);
+      {
+        bf16x8 kop[4];
+        read_k(1, kop);
+        mma_scores(kop, s1);
+        half_weights(s0, m, c, p0, t0s);
+#if !SINKATTN_PREFILL_NO_SCHED
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key_a = 16 * r + 4 * half + (j16 >> 2);
-        const int key_b = key_a + 8;
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const int chunk = 4 * db + 2 * gr_odd + ((j16 & 3) >> 1);
-          const int sub = 8 * (j16 & 1);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_a, chunk) + sub));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_ptr<i16x4>(vs + tile_swizzle(key_b, chunk) + sub));
-          typedef __attribute__((ext_vector_type(8))) short i16x8;
-          vtop[r][db] = __builtin_bit_cast(f16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
         }
+#endif
       }
-      // P^T operands (fp16): operand r covers keys 16r .. 16r+15 of the tile
-      f16x8 pop[2][4];
+      if (__builtin_amdgcn_ballot_w64(t0s[0] > kSumLimit || t0s[1] > kSumLimit) != 0) rebase(0, p0, t0s);
+      dsum[0] += t0s[0];
+      dsum[1] += t0s[1];
+      if (need_mask) mask_half(1, s1);
+      {
+        f16x8 vt[2][2];
+        read_v(0, vt);
+        mma_pv(vt, p0);
+        half_weights(s1, m, c, p1, t1s);
+#if !SINKATTN_PREFILL_NO_SCHED
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        const float m_use = m[rb] == kNegInf ? 0.f : m[rb];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            float pv[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) pv[e] = exp2_hw(__builtin_fmaf(s[kb][rb][8 * hh + e], c, -m_use));
-            u32x4 pk;
-            pk[0] = pack_f16x2(pv[0], pv[1]);
-            pk[1] = pack_f16x2(pv[2], pv[3]);
-            pk[2] = pack_f16x2(pv[4], pv[5]);
-            pk[3] = pack_f16x2(pv[6], pv[7]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dsum[rb] = add_f16x2(pk[e], dsum[rb]);
-            pop[rb][2 * kb + hh] = __builtin_bit_cast(f16x8, pk);
-          }
-      }
-      // O^T += V^T . P^T ; each V^T operand feeds both row blocks
-      mfma_phase_begin();
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          acc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vtop[r][db], pop[0][r], acc[0][db], 0, 0, 0);
-          acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vtop[r][db], pop[1][r], acc[1][db], 0, 0, 0);
+        for (int u = 0; u < 8; ++u) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
         }
-      mfma_phase_end();
+#endif
+      }
+      if (__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit || t1s[1] > kSumLimit) != 0) rebase(1, p1, t1s);
+      dsum[0] += t1s[0];
+      dsum[1] += t1s[1];
+      {
+        f16x8 vt[2][2];
+        read_v(1, vt);
+        mma_pv(vt, p1);
+        reads_then_mfmas<8, 8>();
+      }
     }
 
     if (more) store_tile((it + 1) & 1, kt + kBN, kr, vr);
@@ -390,7 +485,8 @@ void prefill_kernel(PrefillArgs a) {
     const float d = dsum[rb] + shfl_xor_f32(dsum[rb], 32);
     if (my_t[rb] >= n_q) continue;
     float lse2;
-    const float inv = fold_sink(sink2, m[rb], d, &lse2);
+    // every real row sees its own key, so d > 0 here
+    const float inv = fold_sink(sink2, d > 0.f ? m[rb] : kNegInf, d, &lse2);
     const size_t orow = ((size_t)(q_begin + my_t[rb]) * a.num_qo_heads + head) * kHeadDim;
 #pragma unroll
     for (int db = 0; db < 2; ++db)
@@ -420,6 +516,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t str
   return hipGetLastError();
 }
 
-int prefill_rows_per_tile() { return kBM; }
+int prefill_rows_per_tile(int32_t window) {
+  (void)window;
+  return kBM;
+}
 
 }  // namespace sinkattn

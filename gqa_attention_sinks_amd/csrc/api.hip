@@ -245,14 +245,16 @@ int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int3
   int64_t max_len = 0;
   for (int32_t b = 0; b < batch; ++b) max_len = kv_len_host[b] > max_len ? kv_len_host[b] : max_len;
   const int64_t max_pages = (max_len + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE;
-  // aim for about four work units per compute unit (256 CUs), but keep
-  // chunks at least 16 pages long
+  // aim for about eight work units per compute unit (256 CUs): the decode
+  // kernel starts the longest requests first, so the dispatcher can balance
+  // the rest; keep chunks at least 16 pages long, and at most 16 chunks (the
+  // partials and the merge grow with the count)
   const int64_t units = (int64_t)batch * num_kv_heads;
-  int64_t s = (1024 + units - 1) / units;
+  int64_t s = (2048 + units - 1) / units;
   const int64_t cap = max_pages / 16 > 1 ? max_pages / 16 : 1;
   if (s > cap) s = cap;
+  if (s > 16) s = 16;
   if (s < 1) s = 1;
-  if (s > SINKATTN_MAX_SPLITS) s = SINKATTN_MAX_SPLITS;
   return (int32_t)s;
 }
 

@@ -47,16 +47,57 @@ __device__ __forceinline__ int page_swizzle(int key, int chunk) {
   return key * 128 + ((chunk ^ (key & 7)) << 4);
 }
 
-template <int NW, int PPI>
+template <int NW>
 struct DecodeSmem {
-  static constexpr int kStage = NW * PPI * kPageBytes;
+  static constexpr int kStage = NW * kPageBytes;
   static constexpr int kMerge = NW * 16 * (kHeadDim + 2) * 4;
   static constexpr int kBytes = kStage > kMerge ? kStage : kMerge;
 };
 
-template <int NW, int PPI>
+// Requests ranked by KV length (longest first), so that the longest chunks
+// start first and the short ones fill the tail; only for batches up to this
+// size (every workgroup ranks the batch itself).
+constexpr int kRankMaxBatch = 128;
+
+// Work unit of this workgroup: (request b, KV head g, chunk c).  Units are
+// numbered request-major in rank order; within a request the KV heads come
+// first, so consecutive workgroups (and XCDs) share a request's pages.
+template <int NW>
+__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* out_b, int* out_g, int* out_c) {
+  const int S = a.num_splits;
+  int unit = blockIdx.x;
+  const int g = unit % a.num_kv_heads;
+  unit /= a.num_kv_heads;
+  const int c = unit % S;
+  const int r = unit / S;
+  int b = r;
+  if (a.batch <= kRankMaxBatch && a.batch > 1) {
+    __shared__ int s_len[kRankMaxBatch];
+    __shared__ int s_req;
+    for (int i = threadIdx.x; i < a.batch; i += NW * 64) s_len[i] = a.kv_len[i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < a.batch; i += NW * 64) {
+      const int li = s_len[i];
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const int lj = s_len[j];
+        rank += (lj > li) || (lj == li && j < i);
+      }
+      if (rank == r) s_req = i;   // ranks are a permutation: exactly one writer
+    }
+    __syncthreads();
+    b = s_req;
+  }
+  *out_b = b;
+  *out_g = g;
+  *out_c = c;
+}
+
+// PF: pages in flight per wave (a ring of register buffers; the loop is
+// unrolled by PF so the ring slots are static).
+template <int NW, int PF>
 __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, PPI>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW>::kBytes];
 
   const int lane = threadIdx.x & 63;
   // uniform per wave: keeps the page bookkeeping (and the page-id loads) scalar
@@ -65,11 +106,9 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const int grp = lane >> 4;   // 16-lane group
   const int S = a.num_splits;
 
-  int unit = blockIdx.x;
-  const int c = unit % S;
-  unit /= S;
-  const int g = unit % a.num_kv_heads;
-  const int b = unit / a.num_kv_heads;
+  int b, g, c;
+  decode_unit<NW>(a, &b, &g, &c);
+  b = __builtin_amdgcn_readfirstlane(b);
 
   int qrow = b;
   if (a.qo_indptr != nullptr) {
@@ -119,84 +158,74 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
   const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
   const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block
-  uint8_t* stage = smem + wave * (PPI * kPageBytes);
+  uint8_t* stage = smem + wave * kPageBytes;
 
-  // Page ids go through the scalar cache one step before their pages are
-  // fetched, so no vector-memory wait ever blocks on an id while K/V loads
-  // are in flight; K/V of the next step are loaded into registers while the
-  // current step computes.
-  int ids[PPI];
-  auto fetch_ids = [&](int lp) {
-#pragma unroll
-    for (int u = 0; u < PPI; ++u) ids[u] = (lp + u < wp1) ? pages[lp + u] : 0;
-  };
-  u32x4 kc[PPI][2], vc[PPI][2];
-  auto load_step = [&](int lp, u32x4 (&kr)[PPI][2], u32x4 (&vr)[PPI][2]) {
-#pragma unroll
-    for (int u = 0; u < PPI; ++u) {
-      if (lp + u < wp1) {
-        const size_t off = (size_t)ids[u] * page_stride;
-        const uint16_t* kp = kpool + off + lane_off;
-        const uint16_t* vp = vpool + off + lane_off;
-        kr[u][0] = ldg16(kp);
-        kr[u][1] = ldg16(kp + 8);
-        vr[u][0] = ldg16(vp);
-        vr[u][1] = ldg16(vp + 8);
-      }
+  // Ring of PF pages in flight: slot u holds page lp + u of the current
+  // round.  Page ids go through the scalar cache one round ahead of their
+  // loads, so no vector-memory wait ever blocks on an id.
+  u32x4 kc[PF][2], vc[PF][2];
+  int ids[PF];
+  auto fetch_id = [&](int u, int p) { ids[u] = p < wp1 ? pages[p] : 0; };
+  auto load_page = [&](int u, int p) {
+    if (p < wp1) {
+      const size_t off = (size_t)ids[u] * page_stride;
+      const uint16_t* kp = kpool + off + lane_off;
+      const uint16_t* vp = vpool + off + lane_off;
+      kc[u][0] = ldg16(kp);
+      kc[u][1] = ldg16(kp + 8);
+      vc[u][0] = ldg16(vp);
+      vc[u][1] = ldg16(vp + 8);
     }
   };
-  fetch_ids(wp0);
-  if (wp0 < wp1) {
-    load_step(wp0, kc, vc);
-    fetch_ids(wp0 + PPI);
+#pragma unroll
+  for (int u = 0; u < PF; ++u) fetch_id(u, wp0 + u);
+#pragma unroll
+  for (int u = 0; u < PF; ++u) {
+    load_page(u, wp0 + u);
+    fetch_id(u, wp0 + PF + u);
   }
 
-  for (int lp = wp0; lp < wp1; lp += PPI) {
-    u32x4 kn[PPI][2], vn[PPI][2];
-    if (lp + PPI < wp1) {
-      load_step(lp + PPI, kn, vn);
-      fetch_ids(lp + 2 * PPI);
-    }
-
-    // scores of PPI pages
-    float s[PPI][4];
-    float tile_max = kNegInf;
+  for (int lp = wp0; lp < wp1; lp += PF) {
 #pragma unroll
-    for (int u = 0; u < PPI; ++u) {
+    for (int u = 0; u < PF; ++u) {
+      const int p = lp + u;
+      if (p >= wp1) break;
+      // scores of page p (ring slot u)
       f32x4 sc = {};
-      if (lp + u < wp1) {
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), q0, sc, 0, 0, 0);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1, sc, 0, 0, 0);
-      }
-      const int key0 = (lp + u) * kPageSize + 4 * grp;
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), q0, sc, 0, 0, 0);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1, sc, 0, 0, 0);
+      const u32x4 v0r = vc[u][0], v1r = vc[u][1];
+      // the slot is free once its registers are consumed: refill it
+      load_page(u, p + PF);
+      fetch_id(u, p + 2 * PF);
+
+      float s4[4];
+      float tile_max = kNegInf;
+      const int key0 = p * kPageSize + 4 * grp;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int j = key0 + i;
-        const bool vis = (lp + u < wp1) && j >= t_lo && j < t_hi;
-        s[u][i] = vis ? sc[i] * a.scale_log2 : kNegInf;
-        tile_max = fmaxf(tile_max, s[u][i]);
+        const bool vis = j >= t_lo && j < t_hi;
+        s4[i] = vis ? sc[i] * a.scale_log2 : kNegInf;
+        tile_max = fmaxf(tile_max, s4[i]);
       }
-    }
-    tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
-    tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
-    const float m_new = fmaxf(m, tile_max);
-    const float alpha = (m == m_new) ? 1.f : exp2_hw(m - m_new);
-    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-    m = m_new;
-    dsum *= alpha;
+      tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
+      tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
+      const float m_new = fmaxf(m, tile_max);
+      const float alpha = (m == m_new) ? 1.f : exp2_hw(m - m_new);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      m = m_new;
+      dsum *= alpha;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
 
+      float pw[4];
 #pragma unroll
-    for (int u = 0; u < PPI; ++u) {
-      if (lp + u >= wp1) break;
-      float p[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p[i] = exp2_hw(s[u][i] - m_use);
-      const uint32_t p01 = pack_f16x2(p[0], p[1]);
-      const uint32_t p23 = pack_f16x2(p[2], p[3]);
+      for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_use);
+      const uint32_t p01 = pack_f16x2(pw[0], pw[1]);
+      const uint32_t p23 = pack_f16x2(pw[2], pw[3]);
       dsum = add_f16x2(p23, add_f16x2(p01, dsum));
       const f16x4 pb = __builtin_bit_cast(f16x4, u32x2{p01, p23});
 
@@ -205,13 +234,12 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       u32x4 v0, v1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v0[e] = bf16x2_to_f16x2(vc[u][0][e]);
-        v1[e] = bf16x2_to_f16x2(vc[u][1][e]);
+        v0[e] = bf16x2_to_f16x2(v0r[e]);
+        v1[e] = bf16x2_to_f16x2(v1r[e]);
       }
-      if ((lp + u) * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
-      uint8_t* buf = stage + u * kPageBytes;
-      *reinterpret_cast<u32x4*>(buf + page_swizzle(col, 2 * grp)) = v0;
-      *reinterpret_cast<u32x4*>(buf + page_swizzle(col, 2 * grp + 1)) = v1;
+      if (p * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
+      *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp)) = v0;
+      *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp + 1)) = v1;
       __asm__ volatile("" ::: "memory");
       // transposed read: lane (grp, j) addresses key 4*grp + j/4, dims 16*db + 4*(j%4)
       const int rkey = 4 * grp + (col >> 2);
@@ -220,15 +248,10 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
         const int byte = page_swizzle(rkey, 2 * db + ((col & 3) >> 1)) + 8 * (col & 1);
         const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
-                reinterpret_cast<uintptr_t>(buf + byte)));
+                reinterpret_cast<uintptr_t>(stage + byte)));
         acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt), pb, acc[db], 0, 0, 0);
       }
       __asm__ volatile("" ::: "memory");
-    }
-#pragma unroll
-    for (int u = 0; u < PPI; ++u) {
-      kc[u][0] = kn[u][0]; kc[u][1] = kn[u][1];
-      vc[u][0] = vn[u][0]; vc[u][1] = vn[u][1];
     }
   }
 
@@ -308,36 +331,38 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-// Launch shapes: (waves per workgroup, pages per step).  SINKATTN_DECODE_SHAPE
-// ("4x2", "8x4", ...) overrides the default for tuning runs.
-struct DecodeShape { int nw, ppi; };
+// Launch shapes: (waves per workgroup, pages in flight per wave).
+// SINKATTN_DECODE_SHAPE ("4x2", "8x1", ...) overrides the default for tuning
+// runs.
+struct DecodeShape { int nw, pf; };
 
 static DecodeShape decode_shape() {
   static const DecodeShape shape = [] {
     DecodeShape d{4, 1};
     if (const char* e = getenv("SINKATTN_DECODE_SHAPE")) {
-      int nw = 0, ppi = 0;
-      if (sscanf(e, "%dx%d", &nw, &ppi) == 2) d = DecodeShape{nw, ppi};
+      int nw = 0, pf = 0;
+      if (sscanf(e, "%dx%d", &nw, &pf) == 2) d = DecodeShape{nw, pf};
     }
     return d;
   }();
   return shape;
 }
 
-template <int NW, int PPI>
+template <int NW, int PF>
 static void launch_shape(const DecodeArgs& a, long units, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_paged_kernel<NW, PPI>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_paged_kernel<NW, PF>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const long units = (long)a.batch * a.num_kv_heads * a.num_splits;
   if (units <= 0) return hipSuccess;
   const DecodeShape d = decode_shape();
-  if (d.nw == 2 && d.ppi == 4) launch_shape<2, 4>(a, units, stream);
-  else if (d.nw == 4 && d.ppi == 1) launch_shape<4, 1>(a, units, stream);
-  else if (d.nw == 4 && d.ppi == 4) launch_shape<4, 4>(a, units, stream);
-  else if (d.nw == 8 && d.ppi == 2) launch_shape<8, 2>(a, units, stream);
-  else if (d.nw == 8 && d.ppi == 4) launch_shape<8, 4>(a, units, stream);
+  if (d.nw == 4 && d.pf == 1) launch_shape<4, 1>(a, units, stream);
+  else if (d.nw == 4 && d.pf == 3) launch_shape<4, 3>(a, units, stream);
+  else if (d.nw == 4 && d.pf == 4) launch_shape<4, 4>(a, units, stream);
+  else if (d.nw == 8 && d.pf == 1) launch_shape<8, 1>(a, units, stream);
+  else if (d.nw == 8 && d.pf == 2) launch_shape<8, 2>(a, units, stream);
+  else if (d.nw == 2 && d.pf == 4) launch_shape<2, 4>(a, units, stream);
   else launch_shape<4, 2>(a, units, stream);
   return hipGetLastError();
 }

@@ -59,22 +59,31 @@ struct DecodeSmem {
 // size (every workgroup ranks the batch itself).
 constexpr int kRankMaxBatch = 128;
 
-// Work unit of this workgroup: (request b, KV head g, chunk c).  Units are
-// numbered request-major in rank order; within a request the KV heads come
-// first, so consecutive workgroups (and XCDs) share a request's pages.
+// Work unit of this workgroup: (request b, KV head g, chunk c), with the
+// request's KV length and the offset of its page list.  Units are numbered
+// request-major in rank order; within a request the KV heads come first, so
+// consecutive workgroups (and XCDs) share a request's pages.  When ranking,
+// the batch's lengths and page-list offsets are staged in LDS once, so the
+// unit's own metadata costs no further dependent global load.
+struct DecodeUnit { int b, g, c, n_k, page_base; };
+
 template <int NW>
-__device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* out_b, int* out_g, int* out_c) {
+__device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
   const int S = a.num_splits;
   int unit = blockIdx.x;
-  const int g = unit % a.num_kv_heads;
+  DecodeUnit u;
+  u.g = unit % a.num_kv_heads;
   unit /= a.num_kv_heads;
-  const int c = unit % S;
+  u.c = unit % S;
   const int r = unit / S;
-  int b = r;
   if (a.batch <= kRankMaxBatch && a.batch > 1) {
     __shared__ int s_len[kRankMaxBatch];
+    __shared__ int s_ptr[kRankMaxBatch];
     __shared__ int s_req;
-    for (int i = threadIdx.x; i < a.batch; i += NW * 64) s_len[i] = a.kv_len[i];
+    for (int i = threadIdx.x; i < a.batch; i += NW * 64) {
+      s_len[i] = a.kv_len[i];
+      s_ptr[i] = a.page_indptr[i];
+    }
     __syncthreads();
     for (int i = threadIdx.x; i < a.batch; i += NW * 64) {
       const int li = s_len[i];
@@ -86,11 +95,15 @@ __device__ __forceinline__ void decode_unit(const DecodeArgs& a, int* out_b, int
       if (rank == r) s_req = i;   // ranks are a permutation: exactly one writer
     }
     __syncthreads();
-    b = s_req;
+    u.b = s_req;
+    u.n_k = s_len[u.b];
+    u.page_base = s_ptr[u.b];
+  } else {
+    u.b = r;
+    u.n_k = a.kv_len[r];
+    u.page_base = a.page_indptr[r];
   }
-  *out_b = b;
-  *out_g = g;
-  *out_c = c;
+  return u;
 }
 
 // PF: pages in flight per wave (a ring of register buffers; the loop is
@@ -106,9 +119,9 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const int grp = lane >> 4;   // 16-lane group
   const int S = a.num_splits;
 
-  int b, g, c;
-  decode_unit<NW>(a, &b, &g, &c);
-  b = __builtin_amdgcn_readfirstlane(b);
+  const DecodeUnit du = decode_unit<NW>(a);
+  const int b = __builtin_amdgcn_readfirstlane(du.b);
+  const int g = du.g, c = du.c;
 
   int qrow = b;
   if (a.qo_indptr != nullptr) {
@@ -119,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
 
   // Keys this chunk attends to: chunk pages (ceil rule) intersected with the
   // causal / window range of the query at position n_k - 1.
-  const int n_k = a.kv_len[b];
+  const int n_k = __builtin_amdgcn_readfirstlane(du.n_k);
   const int pos = n_k - 1;
   const int lo_vis = a.window > 0 ? max(0, pos - a.window + 1) : 0;
   const int n_pages = (n_k + kPageSize - 1) / kPageSize;
@@ -152,7 +165,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   float m = kNegInf, dsum = 0.f;
   f32x4 acc[4] = {};
 
-  const int32_t* pages = a.page_indices + a.page_indptr[b];
+  const int32_t* pages = a.page_indices + __builtin_amdgcn_readfirstlane(du.page_base);
   const size_t head_stride = (size_t)kPageSize * kHeadDim;          // elements per (page, KV head)
   const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
   const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
@@ -161,14 +174,23 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   uint8_t* stage = smem + wave * kPageBytes;
 
   // Ring of PF pages in flight: slot u holds page lp + u of the current
-  // round.  Page ids go through the scalar cache one round ahead of their
-  // loads, so no vector-memory wait ever blocks on an id.
+  // round.  The wave's page ids arrive as one vector load (lane i holds the
+  // id of page wp0 + 64*k + i, reloaded every 64 pages), issued together
+  // with Q, and each step reads its id with readlane: no per-page scalar load
+  // and only one id latency in front of the first page.
   u32x4 kc[PF][2], vc[PF][2];
-  int ids[PF];
-  auto fetch_id = [&](int u, int p) { ids[u] = p < wp1 ? pages[p] : 0; };
+  int id_vec = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
+  int id_base = wp0;                      // page index of id_vec's lane 0
+  auto page_id = [&](int p) -> int {      // p uniform, wp0 <= p < id_base + 64
+    return __builtin_amdgcn_readlane(id_vec, p - id_base);
+  };
   auto load_page = [&](int u, int p) {
     if (p < wp1) {
-      const size_t off = (size_t)ids[u] * page_stride;
+      if (p - id_base >= 64) {            // uniform: next 64 ids
+        id_base += 64;
+        id_vec = id_base + lane < wp1 ? pages[id_base + lane] : 0;
+      }
+      const size_t off = (size_t)page_id(p) * page_stride;
       const uint16_t* kp = kpool + off + lane_off;
       const uint16_t* vp = vpool + off + lane_off;
       kc[u][0] = ldg16(kp);
@@ -178,12 +200,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     }
   };
 #pragma unroll
-  for (int u = 0; u < PF; ++u) fetch_id(u, wp0 + u);
-#pragma unroll
-  for (int u = 0; u < PF; ++u) {
-    load_page(u, wp0 + u);
-    fetch_id(u, wp0 + PF + u);
-  }
+  for (int u = 0; u < PF; ++u) load_page(u, wp0 + u);
 
   for (int lp = wp0; lp < wp1; lp += PF) {
 #pragma unroll
@@ -197,7 +214,6 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       const u32x4 v0r = vc[u][0], v1r = vc[u][1];
       // the slot is free once its registers are consumed: refill it
       load_page(u, p + PF);
-      fetch_id(u, p + 2 * PF);
 
       float s4[4];
       float tile_max = kNegInf;

@@ -436,14 +436,14 @@ void prefill_kernel(PrefillArgs a) {
         read_k(1, kop);
         mma_scores(kop, s1);
         half_weights(s0, m, c, p0, t0s);
-#if !SINKATTN_PREFILL_NO_SCHED
+        // the step's LDS reads first, then each MFMA followed by a dozen of
+        // the weights' vector instructions
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
         }
-#endif
       }
       if (__builtin_amdgcn_ballot_w64(t0s[0] > kSumLimit || t0s[1] > kSumLimit) != 0) rebase(0, p0, t0s);
       dsum[0] += t0s[0];
@@ -454,14 +454,12 @@ void prefill_kernel(PrefillArgs a) {
         read_v(0, vt);
         mma_pv(vt, p0);
         half_weights(s1, m, c, p1, t1s);
-#if !SINKATTN_PREFILL_NO_SCHED
         __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
         }
-#endif
       }
       if (__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit || t1s[1] > kSumLimit) != 0) rebase(1, p1, t1s);
       dsum[0] += t1s[0];

@@ -116,19 +116,49 @@ __device__ __forceinline__ TileLanes tile_lanes(int lane) {
   return t;
 }
 
-// Find the (request, tile) handled by tile slot `slot`: tiles are numbered
-// request by request; every thread sums a run of requests, then a block scan.
+// Key tiles a query tile spans (the work of a workgroup, in 64-key tiles).
+__device__ __forceinline__ int tile_work(int n_q, int n_k, int t, int window) {
+  const int shift = n_k - n_q;
+  const int t0 = t * kBM;
+  const int t_last = min(t0 + kBM, n_q) - 1;
+  const int lo_first = window > 0 ? max(0, shift + t0 - window + 1) : 0;
+  const int k_first = (lo_first / kBN) * kBN;
+  return (shift + t_last + 1 - k_first + kBN - 1) / kBN;
+}
+
+// Find the (request, tile) handled by tile slot `slot`.  Tiles are numbered
+// request by request (every thread sums a run of requests, then a block
+// scan).  When the requests differ in shape and the batch has at most 256
+// query tiles, the slots take the tiles in order of decreasing work (ties by
+// number), so the longest tiles of every request start first and the short
+// ones fill the tail.  Otherwise they take them request by request, longest
+// tile first: with equal requests that order is as balanced, and tiles of
+// one request that run together share its keys in L2.
 __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* out_b, int* out_tile) {
   constexpr int kThreads = kWaves * 64;
   const int tid = threadIdx.x;
   const int per = (a.batch + kThreads - 1) / kThreads;
   const int b0 = min(tid * per, a.batch);
   const int b1 = min(b0 + per, a.batch);
-  int local = 0;
-  for (int b = b0; b < b1; ++b) {
+  auto req_tiles = [&](int b) {
     const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
-    if (!(a.skip_single_rows && n == 1)) local += (n + kBM - 1) / kBM;
+    return (a.skip_single_rows && n == 1) ? 0 : (n + kBM - 1) / kBM;
+  };
+  auto req_len = [&](int b, int* n_q, int* n_k) {
+    *n_q = a.qo_indptr[b + 1] - a.qo_indptr[b];
+    *n_k = a.paged ? a.kv_len[b] : a.kv_indptr[b + 1] - a.kv_indptr[b];
+  };
+  int local = 0;
+  bool same_shape = true;   // every request shaped like request 0
+  int q0, k0;
+  req_len(0, &q0, &k0);
+  for (int b = b0; b < b1; ++b) {
+    local += req_tiles(b);
+    int nq, nk;
+    req_len(b, &nq, &nk);
+    same_shape = same_shape && nq == q0 && nk == k0;
   }
+  const bool uniform = __syncthreads_and(same_shape);
   s_scan[tid] = local;
   __syncthreads();
   for (int off = 1; off < kThreads; off <<= 1) {
@@ -138,23 +168,56 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
     __syncthreads();
   }
   const int excl = s_scan[tid] - local;
+  const int total = s_scan[kThreads - 1];
   __shared__ int s_found[2];
   if (tid == 0) s_found[0] = -1;
-  __syncthreads();
-  if (slot >= excl && slot < excl + local) {
-    int base = excl;
+  if (total <= kThreads && !uniform) {
+    // list every (request, tile) with its work, then rank
+    __shared__ int s_work[kThreads];
+    __shared__ int s_req[kThreads];
+    __shared__ int s_tile[kThreads];
+    int pos = excl;
     for (int b = b0; b < b1; ++b) {
-      const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
-      const int nt = (a.skip_single_rows && n == 1) ? 0 : (n + kBM - 1) / kBM;
-      if (slot < base + nt) {
-        s_found[0] = b;
-        s_found[1] = nt - 1 - (slot - base);   // longest tile first
-        break;
+      const int nt = req_tiles(b);
+      if (nt == 0) continue;
+      int n_q, n_k;
+      req_len(b, &n_q, &n_k);
+      for (int t = 0; t < nt; ++t, ++pos) {
+        s_work[pos] = tile_work(n_q, n_k, t, a.window);
+        s_req[pos] = b;
+        s_tile[pos] = t;
       }
-      base += nt;
     }
+    __syncthreads();
+    if (tid < total) {
+      const int w = s_work[tid];
+      int rank = 0;
+      for (int q = 0; q < total; ++q) {
+        const int wq = s_work[q];
+        rank += (wq > w) || (wq == w && q < tid);
+      }
+      if (rank == slot) {   // ranks are a permutation: at most one writer
+        s_found[0] = s_req[tid];
+        s_found[1] = s_tile[tid];
+      }
+    }
+    __syncthreads();
+  } else {
+    __syncthreads();
+    if (slot >= excl && slot < excl + local) {
+      int base = excl;
+      for (int b = b0; b < b1; ++b) {
+        const int nt = req_tiles(b);
+        if (slot < base + nt) {
+          s_found[0] = b;
+          s_found[1] = nt - 1 - (slot - base);   // longest tile first
+          break;
+        }
+        base += nt;
+      }
+    }
+    __syncthreads();
   }
-  __syncthreads();
   *out_b = s_found[0];
   *out_tile = s_found[1];
   return s_found[0] >= 0;

@@ -57,7 +57,7 @@ struct DecodeSmem {
 // Requests ranked by KV length (longest first), so that the longest chunks
 // start first and the short ones fill the tail; only for batches up to this
 // size (every workgroup ranks the batch itself).
-constexpr int kRankMaxBatch = 128;
+constexpr int kRankMaxBatch = 256;
 
 // Work unit of this workgroup: (request b, KV head g, chunk c), with the
 // request's KV length and the offset of its page list.  Units are numbered

@@ -211,6 +211,56 @@ def test_mixed_batch_full_size(window):
 
 
 # ---------------------------------------------------------------------------
+# scheduling paths: the work-order logic differs by batch shape, the results
+# must not
+# ---------------------------------------------------------------------------
+
+def test_decode_large_batch_unranked():
+    """300 requests: above the size the decode kernel ranks by length, so
+    units run in natural order."""
+    rng = np.random.default_rng(31)
+    kv_len = rng.integers(1, 300, size=300)
+    w = wl.make_paged("big_batch", kv_len, np.ones(300), 16, 2, rng=rng, decode=True,
+                      sink_overrides=wl.outlier_sinks)
+    say("decode 300 requests (unranked), S in {1, 3}")
+    d = DeviceWorkload(w)
+    ro, rl = oracle_full(w, 0)
+    for s in [1, 3]:
+        out, lse = d.decode(s)
+        assert_parity(to_host(out), ro, f"decode B=300 S={s}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("uniform", [False, True])
+def test_prefill_many_tiles_request_major(uniform):
+    """More than 256 query tiles (uneven or equal requests): the prefill
+    takes tiles request by request instead of ranking them."""
+    rng = np.random.default_rng(32)
+    n = 130
+    qo_len = np.full(n, 300) if uniform else rng.integers(257, 400, size=n)
+    kv_len = qo_len + (0 if uniform else rng.integers(0, 64, size=n))
+    w = wl.make_contiguous("many_tiles", kv_len, qo_len, 4, 1, rng=rng)
+    say(f"prefill {n} requests, {int(np.sum((qo_len + 255) // 256))} tiles, uniform={uniform}")
+    out, lse = DeviceWorkload(w).prefill(window=0)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, f"prefill many tiles uniform={uniform}", to_host(lse), rl)
+
+
+def test_prefill_uneven_ranked_order_windowed():
+    """Uneven requests with at most 256 tiles take the ranked order; also
+    with a window."""
+    rng = np.random.default_rng(33)
+    qo_len = np.array([600, 20, 513, 256, 1000, 3])
+    kv_len = qo_len + np.array([0, 700, 5, 300, 0, 2000])
+    w = wl.make_paged("ranked", kv_len, qo_len, 8, 2, rng=rng)
+    say("prefill uneven requests, ranked order, windows 0 and 200")
+    d = DeviceWorkload(w)
+    for window in [0, 200]:
+        out, lse = d.prefill(window=window)
+        ro, rl = oracle_full(w, window)
+        assert_parity(to_host(out), ro, f"prefill ranked W={window}", to_host(lse), rl)
+
+
+# ---------------------------------------------------------------------------
 # merge entry point
 # ---------------------------------------------------------------------------
 

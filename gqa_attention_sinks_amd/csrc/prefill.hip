@@ -36,6 +36,8 @@
 //   Masking is applied only on tiles that cross the causal diagonal or the
 //   window's lower edge.
 
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
@@ -226,28 +228,30 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
 // fp16 weights of one 32-key half of a tile against the reference m (base 2),
 // packed as P^T operands (pop[rb][hh] covers keys 16*hh .. 16*hh+15 of the
 // half, in the key order of the score accumulator), and this lane's share of
-// each row's weight sum.  The sum is taken over the fp32 weights with plain
-// adds: the packed fp16 dot instruction would occupy the matrix pipe.
+// each row's weight sum.  The sum is taken over the same rounded fp16 weights
+// that feed the P.V product, with a tree of packed fp16 adds (two lanes of
+// eight weights each, 2^-11 relative rounding per level) finished in fp32: the
+// packed fp16 dot instruction would occupy the matrix pipe.  A sum that
+// overflows fp16 comes out as +inf, which the caller's limit check catches.
 __device__ __forceinline__ void half_weights(const f32x16 (&s)[2], const float (&m)[2], float c,
                                              f16x8 (&pop)[2][2], float (&tsum)[2]) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    float part[2] = {0.f, 0.f};
+    f16x2 h[8];
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) {
-      float pv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[e] = exp2_hw(__builtin_fmaf(s[rb][8 * hh + e], c, -m[rb]));
-      u32x4 pk;
-      pk[0] = pack_f16x2(pv[0], pv[1]);
-      pk[1] = pack_f16x2(pv[2], pv[3]);
-      pk[2] = pack_f16x2(pv[4], pv[5]);
-      pk[3] = pack_f16x2(pv[6], pv[7]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) part[e & 1] += pv[e];
-      pop[rb][hh] = __builtin_bit_cast(f16x8, pk);
+    for (int j = 0; j < 8; ++j) {
+      const float lo = exp2_hw(__builtin_fmaf(s[rb][2 * j], c, -m[rb]));
+      const float hi = exp2_hw(__builtin_fmaf(s[rb][2 * j + 1], c, -m[rb]));
+      h[j] = __builtin_bit_cast(f16x2, pack_f16x2(lo, hi));
     }
-    tsum[rb] = part[0] + part[1];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+      pop[rb][hh] = __builtin_bit_cast(f16x8, u32x4{__builtin_bit_cast(uint32_t, h[4 * hh]),
+                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 1]),
+                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 2]),
+                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 3])});
+    const f16x2 t = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+    tsum[rb] = (float)t[0] + (float)t[1];
   }
 }
 
@@ -384,7 +388,22 @@ void prefill_kernel(PrefillArgs a) {
   }
   __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
+  // Lane addresses of the operand reads in stage 0; the stage and the half
+  // tile are compile-time offsets added by the read instructions themselves.
+  uint32_t k_lane[4], v_lane[2][2];
+#pragma unroll
+  for (int kstep = 0; kstep < 4; ++kstep) k_lane[kstep] = opaque(smem0 + tl.k[kstep]);
+#pragma unroll
+  for (int db = 0; db < 2; ++db) {
+    v_lane[db][0] = opaque(smem0 + kTileBytes + tl.v[db][0]);
+    v_lane[db][1] = opaque(smem0 + kTileBytes + tl.v[db][1]);
+  }
+
+  // One key tile; STAGE (the LDS buffer holding it) is a compile-time
+  // constant, so the tile loop below is unrolled by two.
+  auto tile_step = [&](const int it, auto stage_c) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    constexpr uint32_t st = STAGE * 2 * kTileBytes;
     const int kt = k_first + it * kBN;
     u32x4 kr[2], vr[2];
     const bool more = it + 1 < ntiles;
@@ -395,7 +414,6 @@ void prefill_kernel(PrefillArgs a) {
 
     const bool wave_skip = !wave_live || kt > wp_max || (W > 0 && kt + kBN - 1 < wp_min - W + 1);
     if (!wave_skip) {
-      const uint32_t st = smem0 + (it & 1) * 2 * kTileBytes;
       const bool need_mask = (kt + kBN - 1 > wp_min) || (W > 0 && kt < wp_max - W + 1);
       // The tile is processed as two 32-key halves, pipelined inside the
       // wave so that matrix and vector instructions stay independent and can
@@ -406,7 +424,7 @@ void prefill_kernel(PrefillArgs a) {
       auto read_k = [&](int kb, bf16x8 (&kop)[4]) {
 #pragma unroll
         for (int kstep = 0; kstep < 4; ++kstep)
-          kop[kstep] = *lds_at<const bf16x8>(opaque(st + tl.k[kstep]) + kb * 32 * 128);
+          kop[kstep] = *lds_at<const bf16x8>(k_lane[kstep] + (st + kb * 32 * 128));
       };
       auto mma_scores = [&](const bf16x8 (&kop)[4], f32x16 (&sh)[2]) {
         sh[0] = f32x16{};
@@ -434,8 +452,8 @@ void prefill_kernel(PrefillArgs a) {
       auto read_v = [&](int kb, f16x8 (&vt)[2][2]) {   // [hh][db]
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
-          const uint32_t vlo = opaque(st + kTileBytes + tl.v[db][0]);
-          const uint32_t vhi = opaque(st + kTileBytes + tl.v[db][1]);
+          const uint32_t vlo = v_lane[db][0] + st;
+          const uint32_t vhi = v_lane[db][1] + st;
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
             const int r = 2 * kb + hh;
@@ -535,8 +553,12 @@ void prefill_kernel(PrefillArgs a) {
       }
     }
 
-    if (more) store_tile((it + 1) & 1, kt + kBN, kr, vr);
+    if (more) store_tile(STAGE ^ 1, kt + kBN, kr, vr);
     __syncthreads();
+  };
+  for (int it = 0; it < ntiles; it += 2) {
+    tile_step(it, std::integral_constant<int, 0>{});
+    if (it + 1 < ntiles) tile_step(it + 1, std::integral_constant<int, 1>{});
   }
 
   if (!wave_live) return;

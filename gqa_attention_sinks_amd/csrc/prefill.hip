@@ -233,26 +233,38 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
 // eight weights each, 2^-11 relative rounding per level) finished in fp32: the
 // packed fp16 dot instruction would occupy the matrix pipe.  A sum that
 // overflows fp16 comes out as +inf, which the caller's limit check catches.
-__device__ __forceinline__ void half_weights(const f32x16 (&s)[2], const float (&m)[2], float c,
-                                             f16x8 (&pop)[2][2], float (&tsum)[2]) {
+// Weights of scores 2j and 2j+1 of row block rb, packed.
+__device__ __forceinline__ void weight_pair(const f32x16 (&s)[2], const float (&m)[2], float c,
+                                            int rb, int j, f16x2 (&h)[2][8]) {
+  const float lo = exp2_hw(__builtin_fmaf(s[rb][2 * j], c, -m[rb]));
+  const float hi = exp2_hw(__builtin_fmaf(s[rb][2 * j + 1], c, -m[rb]));
+  h[rb][j] = __builtin_bit_cast(f16x2, pack_f16x2(lo, hi));
+}
+
+__device__ __forceinline__ void finish_weights(const f16x2 (&h)[2][8], f16x8 (&pop)[2][2],
+                                               float (&tsum)[2]) {
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    f16x2 h[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float lo = exp2_hw(__builtin_fmaf(s[rb][2 * j], c, -m[rb]));
-      const float hi = exp2_hw(__builtin_fmaf(s[rb][2 * j + 1], c, -m[rb]));
-      h[j] = __builtin_bit_cast(f16x2, pack_f16x2(lo, hi));
-    }
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh)
-      pop[rb][hh] = __builtin_bit_cast(f16x8, u32x4{__builtin_bit_cast(uint32_t, h[4 * hh]),
-                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 1]),
-                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 2]),
-                                                    __builtin_bit_cast(uint32_t, h[4 * hh + 3])});
-    const f16x2 t = ((h[0] + h[1]) + (h[2] + h[3])) + ((h[4] + h[5]) + (h[6] + h[7]));
+      pop[rb][hh] = __builtin_bit_cast(f16x8, u32x4{__builtin_bit_cast(uint32_t, h[rb][4 * hh]),
+                                                    __builtin_bit_cast(uint32_t, h[rb][4 * hh + 1]),
+                                                    __builtin_bit_cast(uint32_t, h[rb][4 * hh + 2]),
+                                                    __builtin_bit_cast(uint32_t, h[rb][4 * hh + 3])});
+    const f16x2 t = ((h[rb][0] + h[rb][1]) + (h[rb][2] + h[rb][3])) +
+                    ((h[rb][4] + h[rb][5]) + (h[rb][6] + h[rb][7]));
     tsum[rb] = (float)t[0] + (float)t[1];
   }
+}
+
+__device__ __forceinline__ void half_weights(const f32x16 (&s)[2], const float (&m)[2], float c,
+                                             f16x8 (&pop)[2][2], float (&tsum)[2]) {
+  f16x2 h[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) weight_pair(s, m, c, rb, j, h);
+  finish_weights(h, pop, tsum);
 }
 
 template <bool PAGED>
@@ -512,19 +524,26 @@ void prefill_kernel(PrefillArgs a) {
         reads_then_mfmas<4, 8>();
       }
       if (need_mask) mask_half(0, s0);
+      // The two overlapped steps are interleaved by hand: each MFMA is
+      // followed by four weights of the other half (fma, exp2, pack), and
+      // scheduling fences keep the compiler from regrouping them, so the
+      // wave issues vector work while its matrix product runs.
       {
         bf16x8 kop[4];
         read_k(1, kop);
-        mma_scores(kop, s1);
-        half_weights(s0, m, c, p0, t0s);
-        // the step's LDS reads first, then each MFMA followed by a dozen of
-        // the weights' vector instructions
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        f16x2 h[2][8];
+        s1[0] = f32x16{};
+        s1[1] = f32x16{};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+          const int kstep = u >> 1, rb = u & 1;
+          s1[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kstep], qop[rb][kstep], s1[rb], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          weight_pair(s0, m, c, u >> 2, 2 * (u & 3), h);
+          weight_pair(s0, m, c, u >> 2, 2 * (u & 3) + 1, h);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        finish_weights(h, p0, t0s);
       }
       if (__builtin_amdgcn_ballot_w64(t0s[0] > kSumLimit || t0s[1] > kSumLimit) != 0) rebase(0, p0, t0s);
       dsum[0] += t0s[0];
@@ -533,14 +552,17 @@ void prefill_kernel(PrefillArgs a) {
       {
         f16x8 vt[2][2];
         read_v(0, vt);
-        mma_pv(vt, p0);
-        half_weights(s1, m, c, p1, t1s);
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        f16x2 h[2][8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+          const int hh = u >> 2, db = (u >> 1) & 1, rb = u & 1;
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[hh][db], p0[rb][hh], acc[rb][db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          weight_pair(s1, m, c, u >> 2, 2 * (u & 3), h);
+          weight_pair(s1, m, c, u >> 2, 2 * (u & 3) + 1, h);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        finish_weights(h, p1, t1s);
       }
       if (__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit || t1s[1] > kSumLimit) != 0) rebase(1, p1, t1s);
       dsum[0] += t1s[0];

@@ -267,47 +267,59 @@ def split_bounds_ref(kv_len, num_splits: int, page_size: int = 16) -> np.ndarray
 
 
 def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, window: int = 0,
-                       sink_in_every_chunk: bool = False, workers: int = 1):
-    """Per-chunk partial results of a one-token-per-request decode ([DAY0-SINK]:
-    the KV sequence is split into blocks and only the first block carries the
-    sink).
+                       sink_in_every_chunk: bool = False, workers: int = 1, qo_indptr=None):
+    """Per-chunk partial results of a decode step ([DAY0-SINK]: the KV sequence
+    is split into blocks and only the first block carries the sink).
 
-    ``q`` is ``[B, Hq, D]``; request ``b``'s query sits at ``kv_len[b] - 1``.
-    For chunk ``c`` with keys ``[lo_c, hi_c)`` (R9) intersected with the visible
-    range (R7), the chunk is attended on its own, its softmax seeded with the
-    sink only when ``c == 0``.  Returns ``o_part [B, Hq, S, D]`` (each chunk
-    normalised by its own Z_c) and ``lse_part [B, Hq, S]`` = ln Z_c.  An empty
+    Without ``qo_indptr``, ``q`` is ``[B, Hq, D]``: one query per request, at
+    position ``kv_len[b] - 1``.  With ``qo_indptr`` ([B+1] row offsets), ``q``
+    is ``[total_q, Hq, D]`` and request ``b`` owns rows ``qo_indptr[b]`` ..
+    ``qo_indptr[b+1] - 1``; its row ``t`` sits at ``kv_len[b] - n_q + t`` (R6),
+    as in a speculative-decoding verify step ([SONAR-INF]: the target model
+    scores several proposed tokens in one pass).  For chunk ``c`` with keys
+    ``[lo_c, hi_c)`` (R9, the request's pages, the same for all its rows)
+    intersected with the row's visible range (R7), the chunk is attended on
+    its own, its softmax seeded with the sink only when ``c == 0``.  Returns
+    ``o_part [rows, Hq, S, D]`` (each chunk normalised by its own Z_c) and
+    ``lse_part [rows, Hq, S]`` = ln Z_c, rows being B or total_q.  An empty
     chunk gives o = 0 with lse = -inf, or lse = sink for chunk 0.
 
     ``sink_in_every_chunk`` exists only as the negative control for tests.
     """
     qf = _as_f64(q)
-    batch, hq, d = qf.shape
+    rows, hq, d = qf.shape
     hkv = kv.k.shape[1]
     group = hq // hkv
     sk = _sinks_f64(sinks, hq)
+    if qo_indptr is None:
+        qo_indptr = np.arange(rows + 1, dtype=np.int64)
+    qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
+    batch = len(qo_indptr) - 1
+    assert int(qo_indptr[-1]) == rows
     kv_len = np.array([kv.length(b) for b in range(batch)])
     bounds = split_bounds_ref(kv_len, num_splits, kv.page_size)
-    o_part = np.zeros((batch, hq, num_splits, d))
-    lse_part = np.empty((batch, hq, num_splits))
+    o_part = np.zeros((rows, hq, num_splits, d))
+    lse_part = np.empty((rows, hq, num_splits))
 
     def unit(bg):
         b, g = bg
         n_k = int(kv_len[b])
-        lo_vis, p = visible_range(1, n_k, 0, window)
-        lo_vis, p = int(lo_vis), int(p)
-        for c in range(num_splits):
-            lo = max(int(bounds[b, c, 0]), lo_vis)
-            hi = min(int(bounds[b, c, 1]), p + 1)
-            kk, vv = kv.rows(b, g, lo, max(lo, hi))
-            for h in range(g * group, (g + 1) * group):
-                seeded = (c == 0) or sink_in_every_chunk
-                sink = np.array([sk[h] if seeded else _NEG_INF])
-                s = scale * (kk @ qf[b, h, :])[None, :]
-                vis = np.ones_like(s, dtype=bool)
-                o, l = _softmax_with_sink(s, vis, sink, vv)
-                o_part[b, h, c, :] = o[0]
-                lse_part[b, h, c] = l[0]
+        r0, r1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
+        for t in range(r1 - r0):
+            lo_vis, p = visible_range(r1 - r0, n_k, t, window)
+            lo_vis, p = int(lo_vis), int(p)
+            for c in range(num_splits):
+                lo = max(int(bounds[b, c, 0]), lo_vis)
+                hi = min(int(bounds[b, c, 1]), p + 1)
+                kk, vv = kv.rows(b, g, lo, max(lo, hi))
+                for h in range(g * group, (g + 1) * group):
+                    seeded = (c == 0) or sink_in_every_chunk
+                    sink = np.array([sk[h] if seeded else _NEG_INF])
+                    s = scale * (kk @ qf[r0 + t, h, :])[None, :]
+                    vis = np.ones_like(s, dtype=bool)
+                    o, l = _softmax_with_sink(s, vis, sink, vv)
+                    o_part[r0 + t, h, c, :] = o[0]
+                    lse_part[r0 + t, h, c] = l[0]
 
     _run_units(unit, [(b, g) for b in range(batch) for g in range(hkv)], workers)
     return o_part, lse_part

@@ -85,3 +85,49 @@ def mp_attention(q, qo_indptr, kvspec, sinks, scale, window, num_kv_heads, dps=5
             out.append(o_row)
             lse.append(l_row)
     return out, lse
+
+
+def brute_split_partials(q, qo_indptr, kvspec, sinks, scale, window, num_kv_heads, num_splits):
+    """Chunk partials of every query row, from the definition: request b's
+    n_pages = ceil(L / page_size) pages are dealt out in order, ceil(n_pages /
+    S) to a chunk; chunk c attends to its own keys that the row can see, with
+    the sink's mass only in chunk 0.  Returns (o_part[row][head][c][dim],
+    lse_part[row][head][c]); a chunk with no mass gives o = 0, lse = -inf."""
+    n_heads = len(sinks)
+    group = n_heads // num_kv_heads
+    ps = kvspec["page_size"]
+    o_part, lse_part = [], []
+    for b in range(len(qo_indptr) - 1):
+        n_q = qo_indptr[b + 1] - qo_indptr[b]
+        n_k = kvspec["kv_len"][b]
+        n_pages = -(-n_k // ps)
+        per = -(-n_pages // num_splits)
+        for t in range(n_q):
+            row = qo_indptr[b] + t
+            pos = n_k - n_q + t
+            first = max(0, pos - window + 1) if window > 0 else 0
+            o_row, l_row = [], []
+            for h in range(n_heads):
+                keys = _key_rows(kvspec, b, h // group)
+                o_h, l_h = [], []
+                for c in range(num_splits):
+                    weights, vals = [], []
+                    for j in range(n_k):
+                        if not (c * per <= j // ps < (c + 1) * per) or not (first <= j <= pos):
+                            continue
+                        kr, vr = keys[j]
+                        weights.append(math.exp(scale * math.fsum(a * e for a, e in zip(q[row][h], kr))))
+                        vals.append(vr)
+                    z = math.fsum(weights + ([math.exp(sinks[h])] if c == 0 else []))
+                    d = len(q[row][h])
+                    if z == 0.0:
+                        o_h.append([0.0] * d)
+                        l_h.append(-math.inf)
+                    else:
+                        o_h.append([math.fsum(w * v[i] for w, v in zip(weights, vals)) / z for i in range(d)])
+                        l_h.append(math.log(z))
+                o_row.append(o_h)
+                l_row.append(l_h)
+            o_part.append(o_row)
+            lse_part.append(l_row)
+    return o_part, lse_part

@@ -51,6 +51,8 @@ def _tiny_problem(rng, paged, batch=None, hq=None, hkv=None, d=None, max_len=9, 
     kv_len = rng.integers(1, max_len + 1, size=batch)
     if qo_mode == "decode":
         qo_len = np.ones(batch, dtype=np.int64)
+    elif qo_mode == "verify":      # a few query rows per request, as in a speculative verify step
+        qo_len = np.array([int(rng.integers(1, min(8, l) + 1)) for l in kv_len])
     else:
         qo_len = np.array([int(rng.integers(1, l + 1)) for l in kv_len])
     qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int64)
@@ -307,6 +309,48 @@ def test_split_equals_unsplit_with_negative_control(seed):
             expect = np.log(np.exp(full_l) + (s - 1) * np.exp(p["sinks"])[None, :])
             np.testing.assert_allclose(lb, expect, rtol=1e-12)
             assert np.max(np.abs(lb - full_l)) > 1e-3
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_multi_row_split_partials_brute_force(seed):
+    rng = np.random.default_rng(9100 + seed)
+    p = _tiny_problem(rng, paged=True, max_len=22, page_size=4, qo_mode="verify")
+    s = int(rng.integers(1, 6))
+    o_part, lse_part = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], s, p["window"],
+                                                 qo_indptr=p["qo_indptr"])
+    bo, bl = _loops.brute_split_partials(p["q"].tolist(), p["qo_indptr"].tolist(), p["spec"],
+                                         p["sinks"].tolist(), p["scale"], p["window"], p["hkv"], s)
+    np.testing.assert_allclose(o_part, np.array(bo), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse_part, np.array(bl), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_multi_row_split_equals_unsplit(seed):
+    rng = np.random.default_rng(9200 + seed)
+    p = _tiny_problem(rng, paged=True, max_len=70, page_size=4, qo_mode="verify")
+    full_o, full_l = _oracle(p)
+    for s in (1, 2, 3, 5, 16):
+        o_part, lse_part = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], s, p["window"],
+                                                     qo_indptr=p["qo_indptr"])
+        out, lse = oracle.merge_ref(o_part, lse_part)
+        np.testing.assert_allclose(out, full_o, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse, full_l, rtol=1e-13, atol=1e-13)
+        if s > 1:
+            o_bad, l_bad = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], s, p["window"],
+                                                     sink_in_every_chunk=True, qo_indptr=p["qo_indptr"])
+            _, lb = oracle.merge_ref(o_bad, l_bad)
+            expect = np.log(np.exp(full_l) + (s - 1) * np.exp(p["sinks"])[None, :])
+            np.testing.assert_allclose(lb, expect, rtol=1e-12)
+
+
+def test_multi_row_with_one_row_requests_is_the_decode_path():
+    rng = np.random.default_rng(9300)
+    p = _tiny_problem(rng, paged=True, batch=3, max_len=40, page_size=4, qo_mode="decode")
+    a = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], 4, p["window"])
+    b = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], 4, p["window"],
+                                  qo_indptr=p["qo_indptr"])
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])
 
 
 def test_gqa_equals_repeated_kv_mha():

@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="paged_decode",
                    choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
-                            "copy_calibration"],
+                            "verify_decode", "copy_calibration"],
                    help="for profiling runs: time only this workload (copy_calibration: a plain "
                         "256 MiB device copy, the reference for HBM byte counters)")
     return p.parse_args()
@@ -64,9 +64,10 @@ def parse():
 # ---------------------------------------------------------------------------
 
 def decode_bytes(w):
-    """K + V of every live key once per KV head, + Q + out + metadata."""
+    """K + V of every live key once per KV head, + Q + out of every query row
+    + metadata."""
     kv = int(np.sum(w.kv_len, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * 2
-    qo = 2 * w.batch * w.num_qo_heads * w.head_dim * 2
+    qo = 2 * int(w.qo_indptr[-1]) * w.num_qo_heads * w.head_dim * 2
     meta = 4 * (len(w.page_indices) + 2 * w.batch + 1)
     return kv + qo + meta
 
@@ -178,6 +179,56 @@ def time_decode(w, args, torch, dev):
     dec_ms = e0.elapsed_time(e1) / args.steps
     mer_ms = e1.elapsed_time(e2) / args.steps if s > 1 else 0.0
     return dict(step_ms=wall * 1e3, decode_ms=dec_ms, merge_ms=mer_ms, splits=s, out=out_host)
+
+
+def time_verify(w, args, torch, dev):
+    """Several query rows per request (sinkattn_decode_paged_multi): the
+    decode kernel alone between two events on its stream, replicas rotated,
+    and the whole step (decode + merge) by wall clock."""
+    import ctypes
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import binding
+    lib = sa.load_library()
+    base = Dev(w, torch, dev)
+    reps = [base] + [base.replica() for _ in range(max(0, args.replicas - 1))]
+    s = args.splits if args.splits > 0 else sa.pick_num_splits(w.kv_len, w.num_kv_heads)
+    B, H, HKV, R = w.batch, w.num_qo_heads, w.num_kv_heads, int(w.meta["max_rows"])
+    TQ = int(w.qo_indptr[-1])
+    outs = [torch.empty_like(r.q) for r in reps]
+    o_part = torch.empty((TQ, H, s, 64), dtype=torch.float32, device=dev)
+    lse_part = torch.empty((TQ, H, s), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len) for r in reps]
+    scale = ctypes.c_float(w.scale)
+    opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
+
+    def call(i, merge):
+        r = reps[i % len(reps)]
+        out = P(outs[i % len(reps)].data_ptr()) if (merge or s == 1) else None
+        st = lib.sinkattn_decode_paged_multi(P(r.q.data_ptr()), P(r.qo_indptr.data_ptr()),
+                                             ctypes.byref(kvs[i % len(reps)]), P(r.sinks.data_ptr()), s, out,
+                                             opart if s > 1 else None, lpart if s > 1 else None, None,
+                                             B, TQ, R, H, HKV, 64, scale, 0, sp)
+        if st != 0:
+            raise RuntimeError(lib.sinkattn_last_error().decode())
+
+    for i in range(args.warmup):
+        call(i, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        call(i, True)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        call(i, False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return dict(step_ms=wall * 1e3, decode_ms=e0.elapsed_time(e1) / args.steps, splits=s)
 
 
 def time_prefill(w, steps, warmup, torch, dev, window=0):
@@ -349,6 +400,13 @@ def profile_only(args, torch, dev, wl):
         return
     w = getattr(wl, args.workload)()
     log(f"timing {args.workload}")
+    if args.workload == "verify_decode":
+        res = time_verify(w, args, torch, dev)
+        gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9
+        print(json.dumps({"workload": args.workload, "rows": int(w.qo_indptr[-1]), "splits": res["splits"],
+                          "step_ms": res["step_ms"], "decode_ms": res["decode_ms"], "decode_GBs": gbs,
+                          "frac": gbs / HBM_PEAK_GBS}))
+        return
     if args.workload == "long_split_decode":
         res = time_decode(w, args, torch, dev)
         gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9

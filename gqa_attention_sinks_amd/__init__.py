@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     SinkAttnError,
     abi_version,
     decode_paged,
+    decode_paged_multi,
     kv_descriptor,
     library_path,
     load_library,

@@ -20,9 +20,11 @@ _LIB = None
 HEAD_DIM = 64
 PAGE_SIZE = 16
 MAX_SPLITS = 256
+MAX_DECODE_ROWS = 8
 EXPORTED = (
     "sinkattn_prefill",
     "sinkattn_decode_paged",
+    "sinkattn_decode_paged_multi",
     "sinkattn_merge",
     "sinkattn_split_bounds",
     "sinkattn_pick_num_splits",
@@ -73,6 +75,9 @@ def load_library():
     lib.sinkattn_decode_paged.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp, i32, i32,
                                           i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged.restype = i32
+    lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp,
+                                                i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.sinkattn_decode_paged_multi.restype = i32
     lib.sinkattn_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge.restype = i32
     lib.sinkattn_split_bounds.argtypes = [vp, i32, i32, i32, vp]
@@ -244,6 +249,56 @@ def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm
                                      _ptr(out if want_out else None), _ptr(o_part), _ptr(lse_part),
                                      _ptr(lse if want_out else None), batch, hq, hkv, HEAD_DIM,
                                      float(sm_scale), int(window), _stream(stream)))
+    if not want_out:
+        return o_part, lse_part
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks,
+                       sm_scale: float, max_qo_len: int, num_splits: int = 1, window: int = 0,
+                       out=None, o_part=None, lse_part=None, lse=None, return_lse: bool = False,
+                       merge: bool = True, stream=None):
+    """Several query rows per request over a paged cache
+    (``sinkattn_decode_paged_multi``); ``q`` is [total_q, Hq, 64] and
+    ``qo_indptr`` [B+1] int32 with 1 .. ``max_qo_len`` rows per request.
+    Partials are per query row: ``o_part`` [total_q, Hq, S, 64], ``lse_part``
+    [total_q, Hq, S].  Returns like :func:`decode_paged`."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [total_q, Hq, 64]")
+    total_q, hq, _ = q.shape
+    _dev(qo_indptr, "qo_indptr", torch.int32)
+    batch = qo_indptr.numel() - 1
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    hkv = k_pool.shape[1]
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32, (hq,))
+    s = int(num_splits)
+    if s > 1:
+        if o_part is None:
+            o_part = torch.empty((total_q, hq, s, HEAD_DIM), dtype=torch.float32, device=q.device)
+        if lse_part is None:
+            lse_part = torch.empty((total_q, hq, s), dtype=torch.float32, device=q.device)
+        _dev(o_part, "o_part", torch.float32, (total_q, hq, s, HEAD_DIM))
+        _dev(lse_part, "lse_part", torch.float32, (total_q, hq, s))
+    else:
+        o_part = lse_part = None
+    want_out = s == 1 or merge
+    if want_out and out is None:
+        out = torch.empty_like(q)
+    if out is not None:
+        _dev(out, "out", torch.bfloat16, q.shape)
+    if want_out and return_lse and lse is None:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (total_q, hq))
+    lib = load_library()
+    _check(lib.sinkattn_decode_paged_multi(_ptr(q), _ptr(qo_indptr), ctypes.byref(kvs), _ptr(sinks), s,
+                                           _ptr(out if want_out else None), _ptr(o_part), _ptr(lse_part),
+                                           _ptr(lse if want_out else None), batch, total_q,
+                                           int(max_qo_len), hq, hkv, HEAD_DIM, float(sm_scale),
+                                           int(window), _stream(stream)))
     if not want_out:
         return o_part, lse_part
     return (out, lse) if (return_lse or lse is not None) else out

@@ -201,6 +201,63 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
   return SINKATTN_OK;
 }
 
+sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,
+                                            const sinkattn_kv* kv, const float* sinks,
+                                            int32_t num_splits, void* out, float* o_part,
+                                            float* lse_part, float* lse, int32_t batch,
+                                            int32_t total_q, int32_t max_qo_len,
+                                            int32_t num_qo_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float sm_scale, int32_t window,
+                                            void* stream) {
+  REQUIRE(q != nullptr && qo_indptr != nullptr, SINKATTN_ERR_INVALID_ARG, "q and qo_indptr are required");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_kv(kv, true)) != SINKATTN_OK) return st;
+  REQUIRE(total_q >= batch, SINKATTN_ERR_INVALID_ARG, "total_q (%d) must be >= batch (%d)", total_q, batch);
+  const int32_t group = num_qo_heads / num_kv_heads;
+  REQUIRE(max_qo_len >= 1 && max_qo_len <= SINKATTN_MAX_DECODE_ROWS, SINKATTN_ERR_INVALID_ARG,
+          "max_qo_len must be in [1, %d] (got %d)", SINKATTN_MAX_DECODE_ROWS, max_qo_len);
+  REQUIRE(group * max_qo_len <= 64, SINKATTN_ERR_UNSUPPORTED,
+          "(Hq/Hkv) * max_qo_len = %d unsupported (at most 64)", group * max_qo_len);
+  REQUIRE(num_splits >= 1 && num_splits <= SINKATTN_MAX_SPLITS, SINKATTN_ERR_INVALID_ARG,
+          "num_splits must be in [1, %d] (got %d)", SINKATTN_MAX_SPLITS, num_splits);
+  if (num_splits == 1) {
+    REQUIRE(out != nullptr, SINKATTN_ERR_INVALID_ARG, "num_splits == 1 needs out");
+  } else {
+    REQUIRE(o_part != nullptr && lse_part != nullptr, SINKATTN_ERR_INVALID_ARG,
+            "num_splits > 1 needs o_part and lse_part");
+  }
+  REQUIRE((long)batch * num_kv_heads * num_splits < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  sinkattn::DecodeArgs d{};
+  d.q = static_cast<const uint16_t*>(q);
+  d.k_pool = static_cast<const uint16_t*>(kv->k);
+  d.v_pool = static_cast<const uint16_t*>(kv->v);
+  d.page_indptr = kv->kv_indptr;
+  d.page_indices = kv->page_indices;
+  d.kv_len = kv->kv_len;
+  d.qo_indptr = qo_indptr;
+  d.sinks = sinks;
+  d.out = static_cast<uint16_t*>(out);
+  d.lse = lse;
+  d.o_part = o_part;
+  d.lse_part = lse_part;
+  d.scale_log2 = sm_scale * 1.4426950408889634f;
+  d.batch = batch;
+  d.num_qo_heads = num_qo_heads;
+  d.num_kv_heads = num_kv_heads;
+  d.group = group;
+  d.num_splits = num_splits;
+  d.window = window;
+  d.max_rows = max_qo_len;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
+  if (num_splits > 1 && out != nullptr) {
+    sinkattn::MergeArgs m{o_part, lse_part, static_cast<uint16_t*>(out), lse, total_q, num_qo_heads, num_splits};
+    if ((st = hip_status(sinkattn::launch_merge(m, s), "merge launch")) != SINKATTN_OK) return st;
+  }
+  return SINKATTN_OK;
+}
+
 sinkattn_status sinkattn_merge(const float* o_part, const float* lse_part, int32_t rows,
                                int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
                                float* lse_out, void* stream) {

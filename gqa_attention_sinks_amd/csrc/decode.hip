@@ -24,6 +24,10 @@
 //        which gives exactly the state of the sink-seeded recurrence.
 //   Each chunk's result is normalised by its own denominator and written as an
 //   fp32 partial with its natural-log LSE, or, unsplit, as the bf16 output.
+//   Several query rows per request (a speculative verify step, "Accelerating
+//   Sonar through speculation", section "Speculative decoding"): the MFMA
+//   columns are (row, head) pairs, up to four 16-column blocks that share
+//   every page load, each column masked at its own causal position.
 
 #include <stdio.h>
 #include <stdlib.h>
@@ -47,10 +51,10 @@ __device__ __forceinline__ int page_swizzle(int key, int chunk) {
   return key * 128 + ((chunk ^ (key & 7)) << 4);
 }
 
-template <int NW>
+template <int NW, int NB>
 struct DecodeSmem {
   static constexpr int kStage = NW * kPageBytes;
-  static constexpr int kMerge = NW * 16 * (kHeadDim + 2) * 4;
+  static constexpr int kMerge = NW * 16 * NB * (kHeadDim + 2) * 4;
   static constexpr int kBytes = kStage > kMerge ? kStage : kMerge;
 };
 
@@ -107,34 +111,49 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
 }
 
 // PF: pages in flight per wave (a ring of register buffers; the loop is
-// unrolled by PF so the ring slots are static).
-template <int NW, int PF>
+// unrolled by PF so the ring slots are static).  NB: 16-column blocks of the
+// MFMAs.  Column j of the blocks is (query row j / G, query head j % G) of
+// the request, so the G heads of one KV head share every page load; one
+// query row per request fills G of the 16 columns of one block, several rows
+// (MULTI: the rows of qo_indptr, as in a speculative verify step) fill up to
+// NB blocks, each column with its own causal limit.
+template <int NW, int PF, int NB, bool MULTI>
 __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW>::kBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, NB>::kBytes];
 
   const int lane = threadIdx.x & 63;
   // uniform per wave: keeps the page bookkeeping (and the page-id loads) scalar
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;   // MFMA column (query head) or row (key) index
+  const int col = lane & 15;   // MFMA column (query row and head) or row (key) index
   const int grp = lane >> 4;   // 16-lane group
   const int S = a.num_splits;
+  const int G = a.group;
 
   const DecodeUnit du = decode_unit<NW>(a);
   const int b = __builtin_amdgcn_readfirstlane(du.b);
   const int g = du.g, c = du.c;
 
-  int qrow = b;
-  if (a.qo_indptr != nullptr) {
+  // the request's first query row and its number of rows
+  int qrow = b, n_q = 1;
+  if (MULTI) {
+    const int r0 = a.qo_indptr[b];
+    qrow = r0;
+    n_q = min(a.qo_indptr[b + 1] - r0, a.max_rows);
+    if (n_q < 1) return;                          // uniform: an empty request
+  } else if (a.qo_indptr != nullptr) {
     const int r0 = a.qo_indptr[b];
     if (a.qo_indptr[b + 1] - r0 != 1) return;   // a prefill request: not ours
     qrow = r0;
   }
+  qrow = __builtin_amdgcn_readfirstlane(qrow);
+  n_q = __builtin_amdgcn_readfirstlane(n_q);
+  // column blocks this request fills (the others are skipped: uniform branches)
+  const int nb_used = MULTI ? (G * n_q + 15) / 16 : 1;
 
   // Keys this chunk attends to: chunk pages (ceil rule) intersected with the
-  // causal / window range of the query at position n_k - 1.
+  // union of the rows' causal / window ranges; row t sits at n_k - n_q + t.
   const int n_k = __builtin_amdgcn_readfirstlane(du.n_k);
-  const int pos = n_k - 1;
-  const int lo_vis = a.window > 0 ? max(0, pos - a.window + 1) : 0;
+  const int lo_vis = a.window > 0 ? max(0, n_k - n_q - a.window + 1) : 0;
   const int n_pages = (n_k + kPageSize - 1) / kPageSize;
   const int ppc = (n_pages + S - 1) / S;
   const int cp0 = min(c * ppc, n_pages);
@@ -147,23 +166,41 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const int wp0 = min(pg0 + wave * per_wave, pg1);
   const int wp1 = min(wp0 + per_wave, pg1);
 
-  const int head = g * a.group + col;
-  const bool head_ok = col < a.group;
-
-  // Q^T operand of the score MFMA: column = head, k = dims 16*grp + 8*ks + e.
-  bf16x8 q0 = {}, q1 = {};
-  if (head_ok) {
-    const uint16_t* qp = a.q + ((size_t)qrow * a.num_qo_heads + head) * kHeadDim + 16 * grp;
-    q0 = __builtin_bit_cast(bf16x8, ldg16(qp));
-    q1 = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
+  // This lane's columns: Q^T operands of the score MFMA (column = (row, head),
+  // k = dims 16*grp + 8*ks + e) and, with several rows, each column's own
+  // visible key range [c_lo, c_pos].
+  bf16x8 q0[NB], q1[NB];
+  int c_lo[NB], c_pos[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = 16 * nb + col;
+    const int t = j / G;
+    const int head = g * G + (j - t * G);
+    q0[nb] = bf16x8{};
+    q1[nb] = bf16x8{};
+    if (t < n_q) {
+      const uint16_t* qp = a.q + ((size_t)(qrow + t) * a.num_qo_heads + head) * kHeadDim + 16 * grp;
+      q0[nb] = __builtin_bit_cast(bf16x8, ldg16(qp));
+      q1[nb] = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
+    }
+    c_pos[nb] = n_k - n_q + t;
+    c_lo[nb] = a.window > 0 ? c_pos[nb] - a.window + 1 : 0;
   }
 
-  // Key-domain streaming state (base 2): running key max, this lane's part of
-  // the denominator, P.V accumulator.  The sink of chunk 0 is folded in once
-  // the waves have merged (fold_sink), giving the state that the recurrence
-  // seeded with (m, d) = (sink, 1) holds after the same keys.
-  float m = kNegInf, dsum = 0.f;
-  f32x4 acc[4] = {};
+  // Key-domain streaming state (base 2) per column block: running key max,
+  // this lane's part of the denominator, P.V accumulator.  The sink of chunk
+  // 0 is folded in once the waves have merged (fold_sink), giving the state
+  // that the recurrence seeded with (m, d) = (sink, 1) holds after the same
+  // keys.
+  float m[NB], dsum[NB];
+  f32x4 acc[NB][4];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    m[nb] = kNegInf;
+    dsum[nb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) acc[nb][db] = f32x4{};
+  }
 
   const int32_t* pages = a.page_indices + __builtin_amdgcn_readfirstlane(du.page_base);
   const size_t head_stride = (size_t)kPageSize * kHeadDim;          // elements per (page, KV head)
@@ -207,43 +244,55 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     for (int u = 0; u < PF; ++u) {
       const int p = lp + u;
       if (p >= wp1) break;
-      // scores of page p (ring slot u)
-      f32x4 sc = {};
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), q0, sc, 0, 0, 0);
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1, sc, 0, 0, 0);
+      // scores of page p (ring slot u), every column block
+      f32x4 sc[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        sc[nb] = f32x4{};
+        if (nb >= nb_used) continue;
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), q0[nb], sc[nb], 0, 0, 0);
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1[nb], sc[nb], 0, 0, 0);
+      }
       const u32x4 v0r = vc[u][0], v1r = vc[u][1];
       // the slot is free once its registers are consumed: refill it
       load_page(u, p + PF);
 
-      float s4[4];
-      float tile_max = kNegInf;
       const int key0 = p * kPageSize + 4 * grp;
+      f16x4 pb[NB];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = key0 + i;
-        const bool vis = j >= t_lo && j < t_hi;
-        s4[i] = vis ? sc[i] * a.scale_log2 : kNegInf;
-        tile_max = fmaxf(tile_max, s4[i]);
-      }
-      tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
-      tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
-      const float m_new = fmaxf(m, tile_max);
-      const float alpha = (m == m_new) ? 1.f : exp2_hw(m - m_new);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      m = m_new;
-      dsum *= alpha;
+      for (int nb = 0; nb < NB; ++nb) {
+        pb[nb] = f16x4{};
+        if (nb >= nb_used) continue;
+        float s4[4];
+        float tile_max = kNegInf;
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+        for (int i = 0; i < 4; ++i) {
+          const int j = key0 + i;
+          bool vis = j >= t_lo && j < t_hi;
+          if (MULTI) vis = vis && j >= c_lo[nb] && j <= c_pos[nb];
+          s4[i] = vis ? sc[nb][i] * a.scale_log2 : kNegInf;
+          tile_max = fmaxf(tile_max, s4[i]);
+        }
+        tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
+        tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
+        const float m_new = fmaxf(m[nb], tile_max);
+        const float alpha = (m[nb] == m_new) ? 1.f : exp2_hw(m[nb] - m_new);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        m[nb] = m_new;
+        dsum[nb] *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[db][i] *= alpha;
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nb][db][i] *= alpha;
 
-      float pw[4];
+        float pw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_use);
-      const uint32_t p01 = pack_f16x2(pw[0], pw[1]);
-      const uint32_t p23 = pack_f16x2(pw[2], pw[3]);
-      dsum = add_f16x2(p23, add_f16x2(p01, dsum));
-      const f16x4 pb = __builtin_bit_cast(f16x4, u32x2{p01, p23});
+        for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_use);
+        const uint32_t p01 = pack_f16x2(pw[0], pw[1]);
+        const uint32_t p23 = pack_f16x2(pw[2], pw[3]);
+        dsum[nb] = add_f16x2(p23, add_f16x2(p01, dsum[nb]));
+        pb[nb] = __builtin_bit_cast(f16x4, u32x2{p01, p23});
+      }
 
       // stage V (natural layout, swizzled); rows past the last key are zeroed
       // so that no stale or poisoned value can meet a zero weight.
@@ -265,56 +314,68 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
         const i16x4 vt = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
             reinterpret_cast<__attribute__((address_space(3))) i16x4*>(
                 reinterpret_cast<uintptr_t>(stage + byte)));
-        acc[db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt), pb, acc[db], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+          if (nb < nb_used)
+            acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt), pb[nb], acc[nb][db], 0, 0, 0);
       }
       __asm__ volatile("" ::: "memory");
     }
   }
 
-  // the four lanes of a head hold partial denominators
-  dsum += shfl_xor_f32(dsum, 16);
-  dsum += shfl_xor_f32(dsum, 32);
+  // the four lanes of a column hold partial denominators
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    dsum[nb] += shfl_xor_f32(dsum[nb], 16);
+    dsum[nb] += shfl_xor_f32(dsum[nb], 32);
+  }
 
   // merge the waves through LDS
+  constexpr int kCols = 16 * NB;
   __syncthreads();
   float* sm_m = reinterpret_cast<float*>(smem);
-  float* sm_d = sm_m + NW * 16;
-  float* sm_o = sm_d + NW * 16;   // [NW][16 heads][64 dims]
-  if (grp == 0) {
-    sm_m[wave * 16 + col] = m;
-    sm_d[wave * 16 + col] = dsum;
-  }
+  float* sm_d = sm_m + NW * kCols;
+  float* sm_o = sm_d + NW * kCols;   // [NW][kCols][64 dims]
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-    *reinterpret_cast<f32x4*>(sm_o + (wave * 16 + col) * kHeadDim + 16 * db + 4 * grp) = acc[db];
+  for (int nb = 0; nb < NB; ++nb) {
+    const int j = 16 * nb + col;
+    if (grp == 0) {
+      sm_m[wave * kCols + j] = m[nb];
+      sm_d[wave * kCols + j] = dsum[nb];
+    }
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      *reinterpret_cast<f32x4*>(sm_o + (wave * kCols + j) * kHeadDim + 16 * db + 4 * grp) = acc[nb][db];
+  }
   __syncthreads();
 
-  for (int idx = threadIdx.x; idx < a.group * kHeadDim; idx += NW * 64) {
-    const int hh = idx / kHeadDim;
+  for (int idx = threadIdx.x; idx < n_q * G * kHeadDim; idx += NW * 64) {
+    const int j = idx / kHeadDim;
     const int d = idx % kHeadDim;
-    const int h = g * a.group + hh;
+    const int t = j / G;
+    const int h = g * G + (j - t * G);
     float mx = kNegInf;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * 16 + hh]);
+    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * kCols + j]);
     float den = 0.f, num = 0.f;
     if (mx != kNegInf) {
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w * 16 + hh];
+        const float mw = sm_m[w * kCols + j];
         const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
-        den += wt * sm_d[w * 16 + hh];
-        num += wt * sm_o[(w * 16 + hh) * kHeadDim + d];
+        den += wt * sm_d[w * kCols + j];
+        num += wt * sm_o[(w * kCols + j) * kHeadDim + d];
       }
     }
     const float sink2 = (c == 0 && a.sinks != nullptr) ? a.sinks[h] * kLog2e : kNegInf;
     float lse2;
     const float o = num * fold_sink(sink2, mx, den, &lse2);
     const float lse_nat = lse2 * kLn2;
+    const size_t rh = (size_t)(qrow + t) * a.num_qo_heads + h;
     if (S == 1) {
-      a.out[((size_t)qrow * a.num_qo_heads + h) * kHeadDim + d] = to_bf16_bits(o);
-      if (a.lse != nullptr && d == 0) a.lse[(size_t)qrow * a.num_qo_heads + h] = lse_nat;
+      a.out[rh * kHeadDim + d] = to_bf16_bits(o);
+      if (a.lse != nullptr && d == 0) a.lse[rh] = lse_nat;
     } else {
-      const size_t rh = (size_t)b * a.num_qo_heads + h;
       a.o_part[(rh * S + c) * kHeadDim + d] = o;
       if (d == 0) a.lse_part[rh * S + c] = lse_nat;
     }
@@ -366,12 +427,20 @@ static DecodeShape decode_shape() {
 
 template <int NW, int PF>
 static void launch_shape(const DecodeArgs& a, long units, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_paged_kernel<NW, PF>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_paged_kernel<NW, PF, 1, false>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const long units = (long)a.batch * a.num_kv_heads * a.num_splits;
   if (units <= 0) return hipSuccess;
+  if (a.max_rows > 0) {   // several query rows per request
+    const int cols = a.group * a.max_rows;
+    const dim3 grid((unsigned)units), block(4 * 64);
+    if (cols <= 16) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, true>), grid, block, 0, stream, a);
+    else if (cols <= 32) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 2, true>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((decode_paged_kernel<4, 1, 4, true>), grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
   const DecodeShape d = decode_shape();
   if (d.nw == 4 && d.pf == 1) launch_shape<4, 1>(a, units, stream);
   else if (d.nw == 4 && d.pf == 3) launch_shape<4, 3>(a, units, stream);

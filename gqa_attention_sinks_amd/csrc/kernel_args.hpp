@@ -7,8 +7,8 @@
 
 namespace sinkattn {
 
-// One query token per request over a paged cache, split into chunks of whole
-// pages; see sinkattn_decode_paged in include/sinkattn.h.
+// Query rows over a paged cache, split into chunks of whole pages; see
+// sinkattn_decode_paged and sinkattn_decode_paged_multi in include/sinkattn.h.
 struct DecodeArgs {
   const uint16_t* q;          // [rows, Hq, 64] bf16
   const uint16_t* k_pool;     // [num_pages, Hkv, 16, 64] bf16
@@ -21,10 +21,13 @@ struct DecodeArgs {
   const float* sinks;         // [Hq] or null
   uint16_t* out;              // num_splits == 1: [rows, Hq, 64] bf16
   float* lse;                 // num_splits == 1: optional [rows, Hq]
-  float* o_part;              // num_splits > 1: [B, Hq, S, 64]
-  float* lse_part;            // num_splits > 1: [B, Hq, S]
+  float* o_part;              // num_splits > 1: [rows, Hq, S, 64] (rows: B, or total_q with max_rows)
+  float* lse_part;            // num_splits > 1: [rows, Hq, S]
   float scale_log2;           // sm_scale * log2(e)
   int32_t batch, num_qo_heads, num_kv_heads, group, num_splits, window;
+  int32_t max_rows;           // 0: one query row per request (above); > 0: request b owns
+                              // rows qo_indptr[b] .. + min(n_b, max_rows) - 1, partials and
+                              // outputs indexed by row
 };
 
 struct MergeArgs {

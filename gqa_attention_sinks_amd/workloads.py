@@ -250,12 +250,25 @@ def mixed_batch(seed=0, n_prefill=16, chunk=512, max_prefix=16384, n_decode=240,
                       windows=(128, 0), meta={"n_prefill": n_prefill, "n_decode": n_decode})
 
 
+def verify_decode(seed=0, batch=64, max_len=4096, min_rows=2, max_rows=8, num_qo_heads=64,
+                  num_kv_heads=8) -> Workload:
+    """A speculative verify step: 64 requests with KV lengths uniform in
+    [max_rows, 4096] (the proposed tokens' keys already cached), each scoring
+    a number of query rows uniform in [2, 8]; 64/8 heads, paged, page size 16."""
+    rng = np.random.default_rng(seed)
+    kv_len = rng.integers(max_rows, max_len + 1, size=batch)
+    qo_len = rng.integers(min_rows, max_rows + 1, size=batch)
+    return make_paged("verify_decode", kv_len, qo_len, num_qo_heads, num_kv_heads, rng=rng,
+                      meta={"max_rows": max_rows})
+
+
 NAMED = {
     "tiny_prefill": tiny_prefill,
     "paged_decode": paged_decode,
     "causal_prefill": causal_prefill,
     "long_split_decode": long_split_decode,
     "mixed_batch": mixed_batch,
+    "verify_decode": verify_decode,
 }
 
 

@@ -57,10 +57,11 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 2
+#define SINKATTN_ABI_VERSION 3
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
+#define SINKATTN_MAX_DECODE_ROWS 8
 
 typedef enum {
   SINKATTN_OK = 0,
@@ -144,6 +145,45 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
                                       int32_t num_qo_heads, int32_t num_kv_heads,
                                       int32_t head_dim, float sm_scale, int32_t window,
                                       void* stream);
+
+/* Several query rows per request over a paged KV cache, split along the KV
+ * sequence like sinkattn_decode_paged: the step in which the target model
+ * scores a few proposed tokens at once ("Accelerating Sonar through
+ * speculation", sections "Speculative decoding" and "Inference with
+ * speculative decoding").  Request b owns query rows qo_indptr[b] ..
+ * qo_indptr[b+1]-1; its row t sits at position kv_len[b] - n_q + t
+ * (bottom-right causal: the proposed tokens' own keys are already in the
+ * cache), and a window W > 0 limits each row to its last W positions.  The
+ * chunks are the request's pages dealt out as in sinkattn_decode_paged (the
+ * same for all of its rows), the sink enters chunk 0 only ("Kernels for
+ * GPT-OSS > Sink attention").  One workgroup per (request, KV head, chunk)
+ * reads each page once for all G = Hq/Hkv heads and all rows of the request.
+ *   q          [total_q, Hq, 64] bf16
+ *   qo_indptr  [batch+1] int32 (device); every request has 1 .. max_qo_len
+ *              rows (rows past max_qo_len are neither read nor written)
+ *   max_qo_len 1 .. SINKATTN_MAX_DECODE_ROWS, with (Hq/Hkv) * max_qo_len <= 64
+ *   kv         paged descriptor (kv->paged must be 1)
+ *   num_splits 1 .. SINKATTN_MAX_SPLITS
+ *   out        num_splits == 1: [total_q, Hq, 64] bf16 (required).
+ *              num_splits > 1: optional; when given, the partials are merged
+ *              into it by a second launch (same as sinkattn_merge over
+ *              total_q rows).
+ *   o_part     num_splits > 1: [total_q, Hq, num_splits, 64] fp32, each chunk
+ *              normalised by its own denominator; empty chunks hold 0.
+ *   lse_part   num_splits > 1: [total_q, Hq, num_splits] fp32 natural-log
+ *              partial LSE: -inf for an empty chunk, the sink for an empty
+ *              chunk 0.  Both ignored (may be NULL) when num_splits == 1.
+ *   lse        optional [total_q, Hq] fp32 final LSE (written with out).
+ * A row whose position is below 0 (n_q > kv_len) sees no key: out = 0,
+ * lse = sink. */
+sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,
+                                            const sinkattn_kv* kv, const float* sinks,
+                                            int32_t num_splits, void* out, float* o_part,
+                                            float* lse_part, float* lse, int32_t batch,
+                                            int32_t total_q, int32_t max_qo_len,
+                                            int32_t num_qo_heads, int32_t num_kv_heads,
+                                            int32_t head_dim, float sm_scale, int32_t window,
+                                            void* stream);
 
 /* Log-sum-exp merge of split partials (the combination implied by splitting
  * the softmax along the KV sequence): per (row, head), with M = max_c lse_c

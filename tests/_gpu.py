@@ -78,6 +78,14 @@ class DeviceWorkload:
                                return_lse=return_lse)
 
 
+    def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True):
+        w = self.w
+        return sa.decode_paged_multi(self.q, self.qo_indptr, self.k, self.v, self.kv_indptr,
+                                     self.page_indices, self.kv_len, self.sinks, w.scale, max_rows,
+                                     num_splits=num_splits, window=window, merge=merge,
+                                     return_lse=return_lse)
+
+
 def kv_cache(w):
     if w.paged:
         return oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr, paged=True,

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 2
+    assert sa.abi_version() == 3
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -145,6 +145,35 @@ def test_decode_argument_errors(lib, kwargs, code):
 
 def test_decode_needs_paged(lib):
     assert _decode(lib, _kv(paged=0)) == INVALID
+
+
+def _decode_multi(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, total_q=6, max_rows=4,
+                  hq=8, hkv=2, d=64, scale=0.125, window=0, q=FAKE, qo=FAKE):
+    return lib.sinkattn_decode_paged_multi(q, qo, ctypes.byref(kv) if kv is not None else None, None, s, out,
+                                           o_part, lse_part, None, batch, total_q, max_rows, hq, hkv, d,
+                                           ctypes.c_float(scale), window, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), INVALID),
+    (dict(qo=None), INVALID),
+    (dict(total_q=1), INVALID),
+    (dict(max_rows=0), INVALID),
+    (dict(max_rows=9), INVALID),
+    (dict(hq=32, hkv=2, max_rows=8), UNSUPPORTED),     # 16 heads x 8 rows > 64 columns
+    (dict(s=0), INVALID),
+    (dict(s=1, out=None), INVALID),
+    (dict(s=4, o_part=None, lse_part=FAKE), INVALID),
+    (dict(d=32), UNSUPPORTED),
+    (dict(window=-1), INVALID),
+])
+def test_decode_multi_argument_errors(lib, kwargs, code):
+    assert _decode_multi(lib, _kv(), **kwargs) == code
+    assert lib.sinkattn_last_error()
+
+
+def test_decode_multi_needs_paged(lib):
+    assert _decode_multi(lib, _kv(paged=0)) == INVALID
 
 
 def test_merge_argument_errors(lib):

@@ -264,6 +264,66 @@ def test_prefill_uneven_ranked_order_windowed():
 # merge entry point
 # ---------------------------------------------------------------------------
 
+# ---------------------------------------------------------------------------
+# several query rows per request (speculative verify) over paged KV
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+def test_verify_decode_full(num_splits):
+    w = wl.verify_decode()
+    say(f"verify_decode full size: B=64 rows~U[2,8] kv~U[8,4096] S={num_splits}")
+    out, lse = DeviceWorkload(w).decode_multi(num_splits, 8)
+    ro, rl = oracle_full(w, 0)
+    assert_parity(to_host(out), ro, f"verify_decode S={num_splits}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("heads,max_rows", [((64, 8), 2), ((4, 1), 8), ((16, 1), 4), ((64, 8), 5)])
+@pytest.mark.parametrize("window", [0, 1, 3, 128])
+def test_verify_decode_shapes_windows(heads, max_rows, window):
+    hq, hkv = heads
+    rng = np.random.default_rng(hq * 100 + max_rows * 10 + window)
+    kv_len = np.array([1, 2, 15, 16, 17, 33, 200, 1000, max_rows, 4097])
+    qo_len = np.minimum(rng.integers(1, max_rows + 1, size=len(kv_len)), kv_len)
+    w = wl.make_paged("verify_edge", kv_len, qo_len, hq, hkv, rng=rng, sink_overrides=wl.outlier_sinks)
+    say(f"verify edges heads={heads} max_rows={max_rows} window={window}")
+    d = DeviceWorkload(w)
+    ro, rl = oracle_full(w, window)
+    for s in [1, 3, 16]:
+        out, lse = d.decode_multi(s, max_rows, window=window)
+        assert_parity(to_host(out), ro, f"verify {heads} R={max_rows} W={window} S={s}", to_host(lse), rl)
+
+
+def test_verify_decode_partials_and_rows_before_the_first_key():
+    """Partials per row (sink only in chunk 0); a request with fewer cached
+    keys than query rows has rows that see no key: out 0, lse = sink."""
+    rng = np.random.default_rng(77)
+    w = wl.make_paged("verify_partials", [300, 40, 5, 700], [4, 7, 5, 1], 64, 8, rng=rng,
+                      sink_overrides=wl.outlier_sinks)
+    w.kv_len = w.kv_len.copy()
+    w.kv_len[2] = 2                      # 5 query rows over 2 keys: rows 0..2 sit before key 0
+    say("verify partials S=4 and rows before the first key")
+    d = DeviceWorkload(w)
+    o_part, lse_part = d.decode_multi(4, 8, merge=False)
+    ro, rl = oracle.split_partials_ref(w.q, kv_cache(w), w.sinks, w.scale, 4, qo_indptr=w.qo_indptr)
+    assert_parity(to_host(o_part), ro, "verify o_part", to_host(lse_part), rl)
+    out, lse = d.decode_multi(1, 8)
+    fo, fl = oracle_full(w, 0)
+    assert_parity(to_host(out), fo, "verify unsplit", to_host(lse), fl)
+
+
+def test_verify_decode_one_row_is_the_decode_kernel():
+    """With one row per request the multi-row path gives the single-token
+    decode kernel's results bit for bit (same arithmetic, same order)."""
+    w = wl.paged_decode(batch=20, max_len=3000)
+    d = DeviceWorkload(w)
+    say("verify one-row vs decode S=1,5")
+    for s in [1, 5]:
+        a, la = d.decode(s)
+        b, lb = d.decode_multi(s, 1)
+        assert np.array_equal(to_host(a), to_host(b)), f"S={s}: outputs differ"
+        assert np.array_equal(to_host(la), to_host(lb)), f"S={s}: LSE differ"
+
+
 def test_merge_entry_point():
     import torch
     import gqa_attention_sinks_amd as sa

@@ -262,6 +262,44 @@ def verify_decode(seed=0, batch=64, max_len=4096, min_rows=2, max_rows=8, num_qo
                       meta={"max_rows": max_rows})
 
 
+def tree_masks(rng, kv_len, qo_len, chain: bool = False):
+    """Draft-tree masks for a verify step (EAGLE-style tree attention): the
+    n_q draft tokens of request b are the last n_q keys of its cache and form
+    a tree (node i's parent a uniformly drawn earlier node, or the prefix);
+    row t sees every prefix key and the draft keys on its own root path.
+    ``chain`` makes every node's parent the previous one (a causal chain).
+    Returns one boolean ``[n_q, n_k]`` array per request."""
+    masks = []
+    for n_k, n_q in zip(np.asarray(kv_len), np.asarray(qo_len)):
+        n_k, n_q = int(n_k), int(n_q)
+        parent = [i - 1 if chain else int(rng.integers(-1, i)) for i in range(n_q)]
+        m = np.zeros((n_q, n_k), dtype=bool)
+        base = n_k - n_q
+        m[:, :max(base, 0)] = True
+        for t in range(n_q):
+            i = t
+            while i >= 0:
+                if base + i >= 0:
+                    m[t, base + i] = True
+                i = parent[i]
+        masks.append(m)
+    return masks
+
+
+def pack_masks(masks):
+    """Bit-pack boolean masks for the library: request b's ``[n_q, n_k]`` mask
+    flattened row-major, bit i of the flat index in byte i // 8 at bit i % 8
+    (little-endian), each request starting on a whole byte.  Returns
+    ``(bits uint8 [nbytes], indptr int32 [B+1])`` with byte offsets."""
+    chunks, indptr = [], [0]
+    for m in masks:
+        packed = np.packbits(np.asarray(m, dtype=bool).reshape(-1), bitorder="little")
+        chunks.append(packed)
+        indptr.append(indptr[-1] + len(packed))
+    bits = np.concatenate(chunks) if chunks else np.zeros(0, dtype=np.uint8)
+    return bits.astype(np.uint8), np.asarray(indptr, dtype=np.int32)
+
+
 NAMED = {
     "tiny_prefill": tiny_prefill,
     "paged_decode": paged_decode,

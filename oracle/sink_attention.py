@@ -42,6 +42,10 @@ Readings of points the pages leave open (each enforced by a test):
 * R10 lse is the natural log of Z and includes the sink.
 * R14 no visible key: o = 0 and lse = sink; sink = +inf: o = 0, lse = +inf;
       sink = -inf and no visible key: o = 0, lse = -inf.
+* R18 custom masks (a draft tree verified in one step): when a boolean mask
+      ``[n_q, n_k]`` is given for a request, key j is visible to row t
+      exactly when ``mask[t, j]``; it replaces the causal rule and the window,
+      and the sink is unchanged (it is no key and is never masked).
 """
 
 from __future__ import annotations
@@ -158,9 +162,11 @@ def _softmax_with_sink(s: np.ndarray, vis: np.ndarray, sink: np.ndarray, vals: n
     return o, lse
 
 
-def _attend_request_group(q_b, kv: KVCache, b: int, g: int, heads, sinks, scale, window, row_block):
+def _attend_request_group(q_b, kv: KVCache, b: int, g: int, heads, sinks, scale, window, row_block,
+                          mask=None):
     """All query rows of request ``b`` for the query heads ``heads`` that read
-    KV head ``g``.  ``q_b`` is fp64 [n_q, Hq, D]."""
+    KV head ``g``.  ``q_b`` is fp64 [n_q, Hq, D]; ``mask`` (optional, bool
+    [n_q, n_k]) replaces the causal / window rule (R18)."""
     n_q = q_b.shape[0]
     n_k = kv.length(b)
     d = q_b.shape[2]
@@ -170,12 +176,18 @@ def _attend_request_group(q_b, kv: KVCache, b: int, g: int, heads, sinks, scale,
     for r0 in range(0, n_q, row_block):
         r1 = min(n_q, r0 + row_block)
         t = np.arange(r0, r1)
-        lo, p = visible_range(n_q, n_k, t, window)
-        k_lo = int(max(0, lo.min()))
-        k_hi = int(min(n_k, p.max() + 1))
+        if mask is None:
+            lo, p = visible_range(n_q, n_k, t, window)
+            k_lo = int(max(0, lo.min()))
+            k_hi = int(min(n_k, p.max() + 1))
+        else:
+            k_lo, k_hi = 0, n_k
         kk, vv = kv.rows(b, g, k_lo, max(k_lo, k_hi))
         j = np.arange(k_lo, k_lo + kk.shape[0])
-        vis = (j[None, :] >= lo[:, None]) & (j[None, :] <= p[:, None])   # [rows, n]
+        if mask is None:
+            vis = (j[None, :] >= lo[:, None]) & (j[None, :] <= p[:, None])   # [rows, n]
+        else:
+            vis = np.asarray(mask, dtype=bool)[r0:r1, k_lo:k_lo + kk.shape[0]]
         for i, h in enumerate(heads):
             s = scale * (q_b[r0:r1, h, :] @ kk.T)
             sink = np.full(r1 - r0, sinks[h])
@@ -194,11 +206,13 @@ def _sinks_f64(sinks, hq):
 
 
 def sink_attention_ref(q, qo_indptr, kv: KVCache, sinks, scale: float, window: int = 0,
-                       workers: int = 1, row_block: int = 256):
+                       workers: int = 1, row_block: int = 256, custom_mask=None):
     """Unsplit sink attention, the plain definition ([DAY0-SINK], [DAY0-HOPPER]).
 
     ``q`` is ``[total_q, Hq, D]`` (bf16 bits or floats), ``qo_indptr`` the
-    ``[B+1]`` row offsets of each request.  Returns fp64 ``out [total_q, Hq, D]``
+    ``[B+1]`` row offsets of each request.  ``custom_mask`` (optional) is one
+    boolean ``[n_q, n_k]`` array per request that replaces the causal rule
+    (R18; ``window`` must then be 0).  Returns fp64 ``out [total_q, Hq, D]``
     and ``lse [total_q, Hq]`` (natural log, sink included).  ``workers`` > 1
     spreads (request, KV head) units over threads, BLAS held to one thread.
     """
@@ -206,6 +220,7 @@ def sink_attention_ref(q, qo_indptr, kv: KVCache, sinks, scale: float, window: i
     total_q, hq, d = qf.shape
     hkv = kv.k.shape[1]
     assert hq % hkv == 0
+    assert custom_mask is None or window == 0
     group = hq // hkv
     sk = _sinks_f64(sinks, hq)
     qo_indptr = np.asarray(qo_indptr, dtype=np.int64)
@@ -219,7 +234,8 @@ def sink_attention_ref(q, qo_indptr, kv: KVCache, sinks, scale: float, window: i
         if r1 == r0:
             return
         heads = list(range(g * group, (g + 1) * group))
-        o, l = _attend_request_group(qf[r0:r1], kv, b, g, heads, sk, scale, window, row_block)
+        mask = None if custom_mask is None else custom_mask[b]
+        o, l = _attend_request_group(qf[r0:r1], kv, b, g, heads, sk, scale, window, row_block, mask)
         out[r0:r1, g * group:(g + 1) * group, :] = o
         lse[r0:r1, g * group:(g + 1) * group] = l
 
@@ -267,7 +283,8 @@ def split_bounds_ref(kv_len, num_splits: int, page_size: int = 16) -> np.ndarray
 
 
 def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, window: int = 0,
-                       sink_in_every_chunk: bool = False, workers: int = 1, qo_indptr=None):
+                       sink_in_every_chunk: bool = False, workers: int = 1, qo_indptr=None,
+                       custom_mask=None):
     """Per-chunk partial results of a decode step ([DAY0-SINK]: the KV sequence
     is split into blocks and only the first block carries the sink).
 
@@ -284,10 +301,15 @@ def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, win
     ``lse_part [rows, Hq, S]`` = ln Z_c, rows being B or total_q.  An empty
     chunk gives o = 0 with lse = -inf, or lse = sink for chunk 0.
 
+    ``custom_mask`` (with ``qo_indptr``): one boolean ``[n_q, n_k]`` array per
+    request replacing the row's visible range (R18); the chunks stay the
+    request's pages.
+
     ``sink_in_every_chunk`` exists only as the negative control for tests.
     """
     qf = _as_f64(q)
     rows, hq, d = qf.shape
+    assert custom_mask is None or (qo_indptr is not None and window == 0)
     hkv = kv.k.shape[1]
     group = hq // hkv
     sk = _sinks_f64(sinks, hq)
@@ -306,8 +328,11 @@ def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, win
         n_k = int(kv_len[b])
         r0, r1 = int(qo_indptr[b]), int(qo_indptr[b + 1])
         for t in range(r1 - r0):
-            lo_vis, p = visible_range(r1 - r0, n_k, t, window)
-            lo_vis, p = int(lo_vis), int(p)
+            if custom_mask is None:
+                lo_vis, p = visible_range(r1 - r0, n_k, t, window)
+                lo_vis, p = int(lo_vis), int(p)
+            else:
+                lo_vis, p = 0, n_k - 1
             for c in range(num_splits):
                 lo = max(int(bounds[b, c, 0]), lo_vis)
                 hi = min(int(bounds[b, c, 1]), p + 1)
@@ -316,7 +341,10 @@ def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, win
                     seeded = (c == 0) or sink_in_every_chunk
                     sink = np.array([sk[h] if seeded else _NEG_INF])
                     s = scale * (kk @ qf[r0 + t, h, :])[None, :]
-                    vis = np.ones_like(s, dtype=bool)
+                    if custom_mask is None:
+                        vis = np.ones_like(s, dtype=bool)
+                    else:
+                        vis = np.asarray(custom_mask[b], dtype=bool)[t, lo:lo + kk.shape[0]][None, :]
                     o, l = _softmax_with_sink(s, vis, sink, vv)
                     o_part[r0 + t, h, c, :] = o[0]
                     lse_part[r0 + t, h, c] = l[0]

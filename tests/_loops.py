@@ -131,3 +131,31 @@ def brute_split_partials(q, qo_indptr, kvspec, sinks, scale, window, num_kv_head
             o_part.append(o_row)
             lse_part.append(l_row)
     return o_part, lse_part
+
+
+def brute_attention_masked(q, qo_indptr, kvspec, sinks, scale, masks, num_kv_heads):
+    """Like brute_attention, with row t of request b seeing key j exactly when
+    masks[b][t][j] (a custom mask replaces the causal rule)."""
+    n_heads = len(sinks)
+    group = n_heads // num_kv_heads
+    out, lse = [], []
+    for b in range(len(qo_indptr) - 1):
+        n_q = qo_indptr[b + 1] - qo_indptr[b]
+        for t in range(n_q):
+            row = qo_indptr[b] + t
+            o_row, l_row = [], []
+            for h in range(n_heads):
+                keys = _key_rows(kvspec, b, h // group)
+                weights, vals = [], []
+                for j, (kr, vr) in enumerate(keys):
+                    if not masks[b][t][j]:
+                        continue
+                    weights.append(math.exp(scale * math.fsum(a * c for a, c in zip(q[row][h], kr))))
+                    vals.append(vr)
+                z = math.fsum(weights + [math.exp(sinks[h])])
+                d = len(q[row][h])
+                o_row.append([math.fsum(w * v[i] for w, v in zip(weights, vals)) / z for i in range(d)])
+                l_row.append(math.log(z))
+            out.append(o_row)
+            lse.append(l_row)
+    return out, lse

@@ -353,6 +353,104 @@ def test_multi_row_with_one_row_requests_is_the_decode_path():
     np.testing.assert_array_equal(a[1], b[1])
 
 
+# ----------------------------------------------------------------------------
+# custom masks (a draft tree verified in one step)
+# ----------------------------------------------------------------------------
+
+def _random_masks(rng, p, density=0.6):
+    qo = p["qo_indptr"]
+    return [rng.random((int(qo[b + 1] - qo[b]), p["kv"].length(b))) < density for b in range(len(qo) - 1)]
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_custom_mask_brute_force(seed):
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(9400 + seed)
+    p = _tiny_problem(rng, paged=bool(seed % 2), max_len=14, page_size=4, qo_mode="verify")
+    qo = p["qo_indptr"]
+    kv_len = [p["kv"].length(b) for b in range(len(qo) - 1)]
+    masks = _random_masks(rng, p) if seed % 2 else wl.tree_masks(rng, kv_len, np.diff(qo))
+    out, lse = oracle.sink_attention_ref(p["q"], qo, p["kv"], p["sinks"], p["scale"], 0, custom_mask=masks)
+    bo, bl = _loops.brute_attention_masked(p["q"].tolist(), qo.tolist(), p["spec"], p["sinks"].tolist(),
+                                           p["scale"], [m.tolist() for m in masks], p["hkv"])
+    np.testing.assert_allclose(out, np.array(bo), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(lse, np.array(bl), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_custom_mask_is_library_attention_when_sink_is_minus_inf(seed):
+    torch = pytest.importorskip("torch")
+    from scipy.special import logsumexp
+    rng = np.random.default_rng(9500 + seed)
+    p = _tiny_problem(rng, paged=True, max_len=30, page_size=4, qo_mode="verify", sink_kind="-inf")
+    qo = p["qo_indptr"]
+    masks = _random_masks(rng, p)
+    for m in masks:
+        m[:, 0] = True           # SDPA needs one visible key per row
+    out, lse = oracle.sink_attention_ref(p["q"], qo, p["kv"], None, p["scale"], 0, custom_mask=masks)
+    hq = p["q"].shape[1]
+    group = hq // p["hkv"]
+    for b in range(len(qo) - 1):
+        kk, vv = zip(*[p["kv"].rows(b, g) for g in range(p["hkv"])])
+        kk = np.stack(kk).repeat(group, axis=0)
+        vv = np.stack(vv).repeat(group, axis=0)
+        qq = p["q"][qo[b]:qo[b + 1]].transpose(1, 0, 2)
+        ro = torch.nn.functional.scaled_dot_product_attention(
+            torch.from_numpy(np.ascontiguousarray(qq)), torch.from_numpy(np.ascontiguousarray(kk)),
+            torch.from_numpy(np.ascontiguousarray(vv)), attn_mask=torch.from_numpy(masks[b]),
+            scale=p["scale"]).numpy().transpose(1, 0, 2)
+        logits = np.where(masks[b][None], p["scale"] * np.matmul(qq, kk.transpose(0, 2, 1)), -np.inf)
+        np.testing.assert_allclose(out[qo[b]:qo[b + 1]], ro, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(lse[qo[b]:qo[b + 1]], logsumexp(logits, axis=-1).T, rtol=1e-12, atol=1e-12)
+
+
+def test_chain_tree_is_causal_and_empty_row_is_the_sink():
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(9600)
+    p = _tiny_problem(rng, paged=True, batch=3, max_len=40, page_size=4, qo_mode="verify")
+    qo = p["qo_indptr"]
+    kv_len = [p["kv"].length(b) for b in range(len(qo) - 1)]
+    chain = wl.tree_masks(rng, kv_len, np.diff(qo), chain=True)
+    full_o, full_l = _oracle(dict(p, window=0))
+    out, lse = oracle.sink_attention_ref(p["q"], qo, p["kv"], p["sinks"], p["scale"], 0, custom_mask=chain)
+    np.testing.assert_allclose(out, full_o, rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(lse, full_l, rtol=1e-14, atol=1e-14)
+    empty = [np.zeros_like(m) for m in chain]
+    out, lse = oracle.sink_attention_ref(p["q"], qo, p["kv"], p["sinks"], p["scale"], 0, custom_mask=empty)
+    assert np.all(out == 0.0)
+    np.testing.assert_array_equal(lse, np.broadcast_to(p["sinks"], lse.shape))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_custom_mask_split_equals_unsplit(seed):
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(9700 + seed)
+    p = _tiny_problem(rng, paged=True, max_len=70, page_size=4, qo_mode="verify")
+    qo = p["qo_indptr"]
+    kv_len = [p["kv"].length(b) for b in range(len(qo) - 1)]
+    masks = wl.tree_masks(rng, kv_len, np.diff(qo))
+    full_o, full_l = oracle.sink_attention_ref(p["q"], qo, p["kv"], p["sinks"], p["scale"], 0, custom_mask=masks)
+    for s in (1, 3, 16):
+        o_part, lse_part = oracle.split_partials_ref(p["q"], p["kv"], p["sinks"], p["scale"], s, qo_indptr=qo,
+                                                     custom_mask=masks)
+        out, lse = oracle.merge_ref(o_part, lse_part)
+        np.testing.assert_allclose(out, full_o, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(lse, full_l, rtol=1e-13, atol=1e-13)
+
+
+def test_mask_packing_round_trip():
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(9800)
+    masks = [rng.random((n_q, n_k)) < 0.5 for n_q, n_k in [(3, 17), (1, 1), (8, 4096), (5, 9)]]
+    bits, indptr = wl.pack_masks(masks)
+    for b, m in enumerate(masks):
+        flat = m.reshape(-1)
+        seg = bits[indptr[b]:indptr[b + 1]]
+        assert len(seg) == (flat.size + 7) // 8
+        for i in rng.integers(0, flat.size, size=min(200, flat.size)):
+            assert bool((seg[i // 8] >> (i % 8)) & 1) == bool(flat[i])
+
+
 def test_gqa_equals_repeated_kv_mha():
     rng = np.random.default_rng(8000)
     p = _tiny_problem(rng, paged=False, batch=2, hq=6, hkv=2, d=4, max_len=12)

@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="paged_decode",
                    choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
-                            "verify_decode", "copy_calibration"],
+                            "verify_decode", "verify_tree", "copy_calibration"],
                    help="for profiling runs: time only this workload (copy_calibration: a plain "
                         "256 MiB device copy, the reference for HBM byte counters)")
     return p.parse_args()
@@ -203,11 +203,18 @@ def time_verify(w, args, torch, dev):
     kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len) for r in reps]
     scale = ctypes.c_float(w.scale)
     opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
+    mask = mask_ptr = None
+    if "masks" in w.meta:            # a draft tree per request (custom mask)
+        from gqa_attention_sinks_amd import workloads as wl
+        bits, indptr = wl.pack_masks(w.meta["masks"])
+        mask_t = torch.from_numpy(bits).to(dev)
+        mask_indptr_t = torch.from_numpy(indptr).to(dev)
+        mask, mask_ptr = P(mask_t.data_ptr()), P(mask_indptr_t.data_ptr())
 
     def call(i, merge):
         r = reps[i % len(reps)]
         out = P(outs[i % len(reps)].data_ptr()) if (merge or s == 1) else None
-        st = lib.sinkattn_decode_paged_multi(P(r.q.data_ptr()), P(r.qo_indptr.data_ptr()),
+        st = lib.sinkattn_decode_paged_multi(P(r.q.data_ptr()), P(r.qo_indptr.data_ptr()), mask, mask_ptr,
                                              ctypes.byref(kvs[i % len(reps)]), P(r.sinks.data_ptr()), s, out,
                                              opart if s > 1 else None, lpart if s > 1 else None, None,
                                              B, TQ, R, H, HKV, 64, scale, 0, sp)
@@ -400,7 +407,7 @@ def profile_only(args, torch, dev, wl):
         return
     w = getattr(wl, args.workload)()
     log(f"timing {args.workload}")
-    if args.workload == "verify_decode":
+    if args.workload in ("verify_decode", "verify_tree"):
         res = time_verify(w, args, torch, dev)
         gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9
         print(json.dumps({"workload": args.workload, "rows": int(w.qo_indptr[-1]), "splits": res["splits"],

@@ -75,8 +75,8 @@ def load_library():
     lib.sinkattn_decode_paged.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp, i32, i32,
                                           i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged.restype = i32
-    lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp,
-                                                i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp,
+                                                vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged_multi.restype = i32
     lib.sinkattn_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge.restype = i32
@@ -257,11 +257,13 @@ def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm
 def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks,
                        sm_scale: float, max_qo_len: int, num_splits: int = 1, window: int = 0,
                        out=None, o_part=None, lse_part=None, lse=None, return_lse: bool = False,
-                       merge: bool = True, stream=None):
+                       merge: bool = True, custom_mask=None, mask_indptr=None, stream=None):
     """Several query rows per request over a paged cache
     (``sinkattn_decode_paged_multi``); ``q`` is [total_q, Hq, 64] and
     ``qo_indptr`` [B+1] int32 with 1 .. ``max_qo_len`` rows per request.
-    Partials are per query row: ``o_part`` [total_q, Hq, S, 64], ``lse_part``
+    ``custom_mask`` (uint8 bit-packed, with int32 byte offsets
+    ``mask_indptr`` [B+1]) replaces the causal rule.  Partials are per query
+    row: ``o_part`` [total_q, Hq, S, 64], ``lse_part``
     [total_q, Hq, S].  Returns like :func:`decode_paged`."""
     torch = _torch()
     _dev(q, "q", torch.bfloat16)
@@ -270,6 +272,9 @@ def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, 
     total_q, hq, _ = q.shape
     _dev(qo_indptr, "qo_indptr", torch.int32)
     batch = qo_indptr.numel() - 1
+    if custom_mask is not None:
+        _dev(custom_mask, "custom_mask", torch.uint8)
+        _dev(mask_indptr, "mask_indptr", torch.int32, (batch + 1,))
     kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
     hkv = k_pool.shape[1]
     if sinks is not None:
@@ -294,7 +299,9 @@ def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, 
     if lse is not None:
         _dev(lse, "lse", torch.float32, (total_q, hq))
     lib = load_library()
-    _check(lib.sinkattn_decode_paged_multi(_ptr(q), _ptr(qo_indptr), ctypes.byref(kvs), _ptr(sinks), s,
+    _check(lib.sinkattn_decode_paged_multi(_ptr(q), _ptr(qo_indptr), _ptr(custom_mask),
+                                           _ptr(mask_indptr if custom_mask is not None else None),
+                                           ctypes.byref(kvs), _ptr(sinks), s,
                                            _ptr(out if want_out else None), _ptr(o_part), _ptr(lse_part),
                                            _ptr(lse if want_out else None), batch, total_q,
                                            int(max_qo_len), hq, hkv, HEAD_DIM, float(sm_scale),

@@ -202,6 +202,7 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
 }
 
 sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,
+                                            const uint8_t* custom_mask, const int32_t* mask_indptr,
                                             const sinkattn_kv* kv, const float* sinks,
                                             int32_t num_splits, void* out, float* o_part,
                                             float* lse_part, float* lse, int32_t batch,
@@ -227,6 +228,10 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
     REQUIRE(o_part != nullptr && lse_part != nullptr, SINKATTN_ERR_INVALID_ARG,
             "num_splits > 1 needs o_part and lse_part");
   }
+  if (custom_mask != nullptr) {
+    REQUIRE(mask_indptr != nullptr, SINKATTN_ERR_INVALID_ARG, "custom_mask needs mask_indptr");
+    REQUIRE(window == 0, SINKATTN_ERR_INVALID_ARG, "a custom mask replaces the window: window must be 0");
+  }
   REQUIRE((long)batch * num_kv_heads * num_splits < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
   sinkattn::DecodeArgs d{};
   d.q = static_cast<const uint16_t*>(q);
@@ -236,6 +241,8 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
   d.page_indices = kv->page_indices;
   d.kv_len = kv->kv_len;
   d.qo_indptr = qo_indptr;
+  d.custom_mask = custom_mask;
+  d.mask_indptr = custom_mask != nullptr ? mask_indptr : nullptr;
   d.sinks = sinks;
   d.out = static_cast<uint16_t*>(out);
   d.lse = lse;

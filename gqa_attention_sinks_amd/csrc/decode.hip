@@ -124,8 +124,10 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
 // the request, so the G heads of one KV head share every page load; one
 // query row per request fills G of the 16 columns of one block, several rows
 // (MULTI: the rows of qo_indptr, as in a speculative verify step) fill up to
-// NB blocks, each column with its own causal limit.
-template <int NW, int PF, int NB, bool MULTI>
+// NB blocks, each column with its own causal limit.  MASK (with MULTI): a
+// bit-packed custom mask per request (a draft tree) decides which keys each
+// row sees, instead of the causal rule.
+template <int NW, int PF, int NB, bool MULTI, bool MASK>
 __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, NB>::kBytes];
 
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   // Keys this chunk attends to: chunk pages (ceil rule) intersected with the
   // union of the rows' causal / window ranges; row t sits at n_k - n_q + t.
   const int n_k = __builtin_amdgcn_readfirstlane(du.n_k);
-  const int lo_vis = a.window > 0 ? max(0, n_k - n_q - a.window + 1) : 0;
+  const int lo_vis = (!MASK && a.window > 0) ? max(0, n_k - n_q - a.window + 1) : 0;
   const int n_pages = (n_k + kPageSize - 1) / kPageSize;
   const int ppc = (n_pages + S - 1) / S;
   const int cp0 = min(c * ppc, n_pages);
@@ -179,6 +181,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   // visible key range [c_lo, c_pos].
   bf16x8 q0[NB], q1[NB];
   int c_lo[NB], c_pos[NB];
+  int c_bit[NB];   // MASK: bit offset of the column's mask row in the request's mask (-1: no row)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int j = 16 * nb + col;
@@ -193,7 +196,10 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     }
     c_pos[nb] = n_k - n_q + t;
     c_lo[nb] = a.window > 0 ? c_pos[nb] - a.window + 1 : 0;
+    c_bit[nb] = t < n_q ? t * n_k : -1;
   }
+  // the request's mask: row t, key j is bit t * n_k + j (little-endian bytes)
+  const uint8_t* mbytes = MASK ? a.custom_mask + a.mask_indptr[b] : nullptr;
 
   // Key-domain streaming state (base 2) per column block: running key max,
   // this lane's part of the denominator, P.V accumulator.  The sink of chunk
@@ -224,6 +230,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   // with Q, and each step reads its id with readlane: no per-page scalar load
   // and only one id latency in front of the first page.
   u32x4 kc[PF][2], vc[PF][2];
+  uint32_t mk[PF][NB];   // MASK: this lane's four mask bits per column block
   int id_vec = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
   int id_base = wp0;                      // page index of id_vec's lane 0
   auto page_id = [&](int p) -> int {      // p uniform, wp0 <= p < id_base + 64
@@ -242,6 +249,22 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       kc[u][1] = ldg16(kp + 8);
       vc[u][0] = ldg16(vp);
       vc[u][1] = ldg16(vp + 8);
+      if (MASK) {
+        // keys key0 .. key0 + 3 of this lane; the bytes read stop at the
+        // request's last key, so they stay inside its mask
+        const int key0 = p * kPageSize + 4 * grp;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          mk[u][nb] = 0;
+          if (nb < nb_used && c_bit[nb] >= 0 && key0 < n_k) {
+            const int bit0 = c_bit[nb] + key0;
+            const int bit1 = c_bit[nb] + min(key0 + 3, n_k - 1);
+            uint32_t w = mbytes[bit0 >> 3];
+            if ((bit1 >> 3) != (bit0 >> 3)) w |= (uint32_t)mbytes[bit1 >> 3] << 8;
+            mk[u][nb] = (w >> (bit0 & 7)) & 0xFu;
+          }
+        }
+      }
     }
   };
 #pragma unroll
@@ -262,6 +285,9 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
         sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1[nb], sc[nb], 0, 0, 0);
       }
       const u32x4 v0r = vc[u][0], v1r = vc[u][1];
+      uint32_t mcur[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) mcur[nb] = MASK ? mk[u][nb] : 0u;
       // the slot is free once its registers are consumed: refill it
       load_page(u, p + PF);
 
@@ -277,7 +303,8 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int j = key0 + i;
           bool vis = j >= t_lo && j < t_hi;
-          if (MULTI) vis = vis && j >= c_lo[nb] && j <= c_pos[nb];
+          if (MASK) vis = vis && ((mcur[nb] >> i) & 1u);
+          else if (MULTI) vis = vis && j >= c_lo[nb] && j <= c_pos[nb];
           s4[i] = vis ? sc[nb][i] * a.scale_log2 : kNegInf;
           tile_max = fmaxf(tile_max, s4[i]);
         }
@@ -435,7 +462,7 @@ static DecodeShape decode_shape() {
 
 template <int NW, int PF>
 static void launch_shape(const DecodeArgs& a, long units, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_paged_kernel<NW, PF, 1, false>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_paged_kernel<NW, PF, 1, false, false>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -444,9 +471,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.max_rows > 0) {   // several query rows per request
     const int cols = a.group * a.max_rows;
     const dim3 grid((unsigned)units), block(4 * 64);
-    if (cols <= 16) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, true>), grid, block, 0, stream, a);
-    else if (cols <= 32) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 2, true>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((decode_paged_kernel<4, 1, 4, true>), grid, block, 0, stream, a);
+    if (a.custom_mask != nullptr) {
+      if (cols <= 16) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, true, true>), grid, block, 0, stream, a);
+      else if (cols <= 32) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 2, true, true>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_paged_kernel<4, 1, 4, true, true>), grid, block, 0, stream, a);
+    } else {
+      if (cols <= 16) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, true, false>), grid, block, 0, stream, a);
+      else if (cols <= 32) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 2, true, false>), grid, block, 0, stream, a);
+      else hipLaunchKernelGGL((decode_paged_kernel<4, 1, 4, true, false>), grid, block, 0, stream, a);
+    }
     return hipGetLastError();
   }
   const DecodeShape d = decode_shape();

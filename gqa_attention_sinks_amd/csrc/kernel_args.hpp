@@ -28,6 +28,8 @@ struct DecodeArgs {
   int32_t max_rows;           // 0: one query row per request (above); > 0: request b owns
                               // rows qo_indptr[b] .. + min(n_b, max_rows) - 1, partials and
                               // outputs indexed by row
+  const uint8_t* custom_mask; // optional with max_rows: bit t * n_k + j of request b's bytes
+  const int32_t* mask_indptr; // (from mask_indptr[b]) = row t sees key j
 };
 
 struct MergeArgs {

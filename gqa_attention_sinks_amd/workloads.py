@@ -262,6 +262,15 @@ def verify_decode(seed=0, batch=64, max_len=4096, min_rows=2, max_rows=8, num_qo
                       meta={"max_rows": max_rows})
 
 
+def verify_tree(seed=0) -> Workload:
+    """The verify batch of ``verify_decode`` with a random draft tree per
+    request (its custom mask in ``meta["masks"]``)."""
+    w = verify_decode(seed)
+    rng = np.random.default_rng(seed + 1)
+    w.meta["masks"] = tree_masks(rng, w.kv_len, np.diff(w.qo_indptr))
+    return w
+
+
 def tree_masks(rng, kv_len, qo_len, chain: bool = False):
     """Draft-tree masks for a verify step (EAGLE-style tree attention): the
     n_q draft tokens of request b are the last n_q keys of its cache and form
@@ -307,6 +316,7 @@ NAMED = {
     "long_split_decode": long_split_decode,
     "mixed_batch": mixed_batch,
     "verify_decode": verify_decode,
+    "verify_tree": verify_tree,
 }
 
 

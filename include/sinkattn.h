@@ -161,6 +161,16 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
  *   q          [total_q, Hq, 64] bf16
  *   qo_indptr  [batch+1] int32 (device); every request has 1 .. max_qo_len
  *              rows (rows past max_qo_len are neither read nor written)
+ *   custom_mask optional (device, NULL = the causal rule above): a draft
+ *              tree verified in one step (tree attention, "Accelerating
+ *              Sonar through speculation", section "Speculative decoding":
+ *              the target scores the drafted tokens in one pass).  Request b's
+ *              mask starts at byte mask_indptr[b]; bit t * kv_len[b] + j of it
+ *              (bit i in byte i / 8 at position i % 8) says whether row t
+ *              sees key j.  It replaces the causal rule and needs window == 0;
+ *              the sink is not a key and is never masked.  A row with no
+ *              visible key gets out = 0, lse = sink.
+ *   mask_indptr [batch+1] int32 byte offsets (device), required with custom_mask
  *   max_qo_len 1 .. SINKATTN_MAX_DECODE_ROWS, with (Hq/Hkv) * max_qo_len <= 64
  *   kv         paged descriptor (kv->paged must be 1)
  *   num_splits 1 .. SINKATTN_MAX_SPLITS
@@ -177,6 +187,7 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
  * A row whose position is below 0 (n_q > kv_len) sees no key: out = 0,
  * lse = sink. */
 sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,
+                                            const uint8_t* custom_mask, const int32_t* mask_indptr,
                                             const sinkattn_kv* kv, const float* sinks,
                                             int32_t num_splits, void* out, float* o_part,
                                             float* lse_part, float* lse, int32_t batch,

@@ -78,12 +78,19 @@ class DeviceWorkload:
                                return_lse=return_lse)
 
 
-    def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True):
+    def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True, masks=None):
         w = self.w
+        mask = mask_indptr = None
+        if masks is not None:
+            from gqa_attention_sinks_amd import workloads as wl
+            bits, indptr = wl.pack_masks(masks)
+            torch, dev = torch_dev()
+            mask = torch.from_numpy(bits).to(dev)
+            mask_indptr = i32_to_dev(indptr)
         return sa.decode_paged_multi(self.q, self.qo_indptr, self.k, self.v, self.kv_indptr,
                                      self.page_indices, self.kv_len, self.sinks, w.scale, max_rows,
                                      num_splits=num_splits, window=window, merge=merge,
-                                     return_lse=return_lse)
+                                     return_lse=return_lse, custom_mask=mask, mask_indptr=mask_indptr)
 
 
 def kv_cache(w):

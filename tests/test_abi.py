@@ -148,8 +148,9 @@ def test_decode_needs_paged(lib):
 
 
 def _decode_multi(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, total_q=6, max_rows=4,
-                  hq=8, hkv=2, d=64, scale=0.125, window=0, q=FAKE, qo=FAKE):
-    return lib.sinkattn_decode_paged_multi(q, qo, ctypes.byref(kv) if kv is not None else None, None, s, out,
+                  hq=8, hkv=2, d=64, scale=0.125, window=0, q=FAKE, qo=FAKE, mask=None, mask_indptr=None):
+    return lib.sinkattn_decode_paged_multi(q, qo, mask, mask_indptr,
+                                           ctypes.byref(kv) if kv is not None else None, None, s, out,
                                            o_part, lse_part, None, batch, total_q, max_rows, hq, hkv, d,
                                            ctypes.c_float(scale), window, None)
 
@@ -166,6 +167,8 @@ def _decode_multi(lib, kv, s=1, out=FAKE, o_part=None, lse_part=None, batch=2, t
     (dict(s=4, o_part=None, lse_part=FAKE), INVALID),
     (dict(d=32), UNSUPPORTED),
     (dict(window=-1), INVALID),
+    (dict(mask=FAKE, mask_indptr=None), INVALID),
+    (dict(mask=FAKE, mask_indptr=FAKE, window=8), INVALID),
 ])
 def test_decode_multi_argument_errors(lib, kwargs, code):
     assert _decode_multi(lib, _kv(), **kwargs) == code

@@ -324,6 +324,59 @@ def test_verify_decode_one_row_is_the_decode_kernel():
         assert np.array_equal(to_host(la), to_host(lb)), f"S={s}: LSE differ"
 
 
+# ---------------------------------------------------------------------------
+# custom masks: a draft tree per request verified in one step
+# ---------------------------------------------------------------------------
+
+def _oracle_masked(w, masks):
+    return oracle.sink_attention_ref(w.q, w.qo_indptr, kv_cache(w), w.sinks, w.scale, 0, workers=8,
+                                     custom_mask=masks)
+
+
+@pytest.mark.parametrize("num_splits", [1, 3, 16])
+def test_tree_verify_full(num_splits):
+    w = wl.verify_tree()
+    say(f"verify_tree full size: B=64 rows~U[2,8] random draft trees S={num_splits}")
+    out, lse = DeviceWorkload(w).decode_multi(num_splits, 8, masks=w.meta["masks"])
+    ro, rl = _oracle_masked(w, w.meta["masks"])
+    assert_parity(to_host(out), ro, f"verify_tree S={num_splits}", to_host(lse), rl)
+
+
+@pytest.mark.parametrize("heads,max_rows", [((64, 8), 8), ((4, 1), 8), ((16, 1), 4), ((64, 8), 2)])
+def test_custom_mask_random_and_edges(heads, max_rows):
+    hq, hkv = heads
+    rng = np.random.default_rng(hq * 1000 + max_rows)
+    kv_len = np.array([1, 2, 15, 16, 17, 33, 200, 1000, max_rows, 4097])
+    qo_len = np.minimum(rng.integers(1, max_rows + 1, size=len(kv_len)), kv_len)
+    w = wl.make_paged("mask_edge", kv_len, qo_len, hq, hkv, rng=rng, sink_overrides=wl.outlier_sinks)
+    masks = [rng.random((int(q), int(k))) < 0.5 for q, k in zip(qo_len, kv_len)]
+    masks[3][0, :] = False            # a row that sees no key: out 0, lse = sink
+    say(f"random masks heads={heads} max_rows={max_rows}")
+    d = DeviceWorkload(w)
+    ro, rl = _oracle_masked(w, masks)
+    for s in [1, 3]:
+        out, lse = d.decode_multi(s, max_rows, masks=masks)
+        assert_parity(to_host(out), ro, f"mask {heads} R={max_rows} S={s}", to_host(lse), rl)
+    o_part, lse_part = d.decode_multi(4, max_rows, merge=False, masks=masks)
+    po, pl = oracle.split_partials_ref(w.q, kv_cache(w), w.sinks, w.scale, 4, qo_indptr=w.qo_indptr,
+                                       custom_mask=masks)
+    assert_parity(to_host(o_part), po, f"mask partials {heads}", to_host(lse_part), pl)
+
+
+def test_chain_mask_is_the_causal_kernel():
+    """A chain-shaped draft tree is the causal rule: the masked kernel gives
+    the unmasked one's results bit for bit."""
+    w = wl.verify_decode(batch=24, max_len=3000)
+    masks = wl.tree_masks(np.random.default_rng(5), w.kv_len, np.diff(w.qo_indptr), chain=True)
+    d = DeviceWorkload(w)
+    say("chain mask vs causal S=1,4")
+    for s in [1, 4]:
+        a, la = d.decode_multi(s, 8)
+        b, lb = d.decode_multi(s, 8, masks=masks)
+        assert np.array_equal(to_host(a), to_host(b)), f"S={s}: outputs differ"
+        assert np.array_equal(to_host(la), to_host(lb)), f"S={s}: LSE differ"
+
+
 def test_merge_entry_point():
     import torch
     import gqa_attention_sinks_amd as sa

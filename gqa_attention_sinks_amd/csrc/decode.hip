@@ -39,6 +39,10 @@ namespace sinkattn {
 namespace {
 
 constexpr int kPageBytes = kPageSize * kHeadDim * 2;  // one (page, KV head) block: 2 KiB
+// fp16 weights are taken against a reference that moves only when some weight
+// would exceed this (fp16 keeps them finite, the rescale stays rare)
+constexpr float kWeightLimit = 16384.f;
+constexpr float kFloatMax = 3.402823466e38f;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -175,6 +179,9 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   const int per_wave = (pg1 - pg0 + NW - 1) / NW;
   const int wp0 = min(pg0 + wave * per_wave, pg1);
   const int wp1 = min(wp0 + per_wave, pg1);
+  // keys every row of the request sees: [full_lo, full_hi] within the chunk
+  const int full_lo = a.window > 0 ? max(t_lo, n_k - a.window) : t_lo;
+  const int full_hi = min(t_hi - 1, n_k - n_q);
 
   // This lane's columns: Q^T operands of the score MFMA (column = (row, head),
   // k = dims 16*grp + 8*ks + e) and, with several rows, each column's own
@@ -210,7 +217,7 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   f32x4 acc[NB][4];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    m[nb] = kNegInf;
+    m[nb] = -kFloatMax;
     dsum[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < 4; ++db) acc[nb][db] = f32x4{};
@@ -292,37 +299,74 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       load_page(u, p + PF);
 
       const int key0 = p * kPageSize + 4 * grp;
+      // uniform: every key of the page visible to every column (no per-key test)
+      const bool page_full = !MASK && p * kPageSize >= full_lo && p * kPageSize + kPageSize - 1 <= full_hi;
       f16x4 pb[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
         pb[nb] = f16x4{};
         if (nb >= nb_used) continue;
-        float s4[4];
-        float tile_max = kNegInf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        auto visible = [&](int i) -> bool {
           const int j = key0 + i;
           bool vis = j >= t_lo && j < t_hi;
           if (MASK) vis = vis && ((mcur[nb] >> i) & 1u);
           else if (MULTI) vis = vis && j >= c_lo[nb] && j <= c_pos[nb];
-          s4[i] = vis ? sc[nb][i] * a.scale_log2 : kNegInf;
-          tile_max = fmaxf(tile_max, s4[i]);
-        }
-        tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
-        tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
-        const float m_new = fmaxf(m[nb], tile_max);
-        const float alpha = (m[nb] == m_new) ? 1.f : exp2_hw(m[nb] - m_new);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        m[nb] = m_new;
-        dsum[nb] *= alpha;
+          return vis;
+        };
+        // scaled scores (base 2) of the lane's four keys, -inf where not visible
+        auto masked_scores = [&](float (&s4)[4]) {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nb][db][i] *= alpha;
-
+          for (int i = 0; i < 4; ++i) s4[i] = visible(i) ? sc[nb][i] * a.scale_log2 : kNegInf;
+        };
         float pw[4];
+        if constexpr (MULTI) {
+          // Weights against the current reference m (the same arithmetic on
+          // every visible key, whichever the path).  A weight above the limit
+          // means a key well above the reference (always on a wave's first
+          // visible page, m starting at -FLT_MAX): move the reference to the
+          // column maxima, rescale, and redo the weights.
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_use);
+          for (int i = 0; i < 4; ++i) {
+            pw[i] = exp2_hw(__builtin_fmaf(sc[nb][i], a.scale_log2, -m[nb]));
+            if (!page_full && !visible(i)) pw[i] = 0.f;
+          }
+          const float pmax = fmaxf(fmaxf(pw[0], pw[1]), fmaxf(pw[2], pw[3]));
+          if (__builtin_amdgcn_ballot_w64(pmax > kWeightLimit) != 0) {
+            float s4[4];
+            masked_scores(s4);
+            float tile_max = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+            tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
+            tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
+            const float m_new = fmaxf(m[nb], tile_max);
+            const float alpha = exp2_hw(m[nb] - m_new);
+            m[nb] = m_new;
+            dsum[nb] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[nb][db][i] *= alpha;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_new);
+          }
+        } else {
+          // one row: the running maximum moves with every page (the kernel is
+          // bound by the page gathers, and this form holds fewer registers)
+          float s4[4];
+          masked_scores(s4);
+          float tile_max = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+          tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
+          tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));
+          const float m_new = fmaxf(m[nb], tile_max);
+          const float alpha = (m[nb] == m_new) ? 1.f : exp2_hw(m[nb] - m_new);
+          m[nb] = m_new;
+          dsum[nb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[nb][db][i] *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(s4[i] - m_new);
+        }
         const uint32_t p01 = pack_f16x2(pw[0], pw[1]);
         const uint32_t p23 = pack_f16x2(pw[2], pw[3]);
         dsum[nb] = add_f16x2(p23, add_f16x2(p01, dsum[nb]));
@@ -389,22 +433,22 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     const int d = idx % kHeadDim;
     const int t = j / G;
     const int h = g * G + (j - t * G);
-    float mx = kNegInf;
+    // each wave's reference is finite (-FLT_MAX until its first visible key)
+    float mx = -kFloatMax;
 #pragma unroll
     for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * kCols + j]);
     float den = 0.f, num = 0.f;
-    if (mx != kNegInf) {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float mw = sm_m[w * kCols + j];
-        const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
-        den += wt * sm_d[w * kCols + j];
-        num += wt * sm_o[(w * kCols + j) * kHeadDim + d];
-      }
+    for (int w = 0; w < NW; ++w) {
+      const float mw = sm_m[w * kCols + j];
+      const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
+      den += wt * sm_d[w * kCols + j];
+      num += wt * sm_o[(w * kCols + j) * kHeadDim + d];
     }
     const float sink2 = (c == 0 && a.sinks != nullptr) ? a.sinks[h] * kLog2e : kNegInf;
     float lse2;
-    const float o = num * fold_sink(sink2, mx, den, &lse2);
+    // no visible key in the chunk: the key part is empty (d = 0)
+    const float o = num * fold_sink(sink2, den > 0.f ? mx : kNegInf, den, &lse2);
     const float lse_nat = lse2 * kLn2;
     const size_t rh = (size_t)(qrow + t) * a.num_qo_heads + h;
     if (S == 1) {

@@ -311,17 +311,20 @@ def test_verify_decode_partials_and_rows_before_the_first_key():
     assert_parity(to_host(out), fo, "verify unsplit", to_host(lse), fl)
 
 
-def test_verify_decode_one_row_is_the_decode_kernel():
-    """With one row per request the multi-row path gives the single-token
-    decode kernel's results bit for bit (same arithmetic, same order)."""
+def test_verify_decode_one_row_matches_the_decode_kernel():
+    """With one row per request the multi-row kernel (whose softmax reference
+    moves only on overflow) and the single-token kernel (running maximum)
+    both meet the parity bar and agree with each other to it."""
     w = wl.paged_decode(batch=20, max_len=3000)
     d = DeviceWorkload(w)
+    ro, rl = oracle_full(w, 0)
     say("verify one-row vs decode S=1,5")
     for s in [1, 5]:
         a, la = d.decode(s)
         b, lb = d.decode_multi(s, 1)
-        assert np.array_equal(to_host(a), to_host(b)), f"S={s}: outputs differ"
-        assert np.array_equal(to_host(la), to_host(lb)), f"S={s}: LSE differ"
+        assert_parity(to_host(b), ro, f"one-row multi S={s}", to_host(lb), rl)
+        assert_parity(to_host(a), ro, f"decode S={s}", to_host(la), rl)
+        assert_parity(to_host(b), to_host(a), f"multi vs decode S={s}", to_host(lb), to_host(la))
 
 
 # ---------------------------------------------------------------------------

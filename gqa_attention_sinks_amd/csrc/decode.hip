@@ -461,7 +461,36 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   }
 }
 
-// One wave per (row, head); lane = output dimension.
+// One wave per (row, head); lane = output dimension.  With at most N chunks
+// (N = 4, 8 or 16, the smallest that fits) every load -- the chunk LSEs and
+// this lane's value of each partial -- is issued before the first use, so
+// the wave waits for one memory round trip instead of one per chunk; more
+// chunks take the plain loop.
+template <int N>
+__device__ __forceinline__ void merge_regs(const float* lp, const float* op, int S, float& mx,
+                                           float& den, float& num) {
+  float l[N], o[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) {   // index clamped to chunk S - 1: straight-line loads
+    const int cc = min(c, S - 1);
+    l[c] = lp[cc];
+    o[c] = op[(long)cc * kHeadDim];
+  }
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (c >= S) l[c] = kNegInf;
+    mx = fmaxf(mx, l[c]);
+  }
+  if (mx == kNegInf) return;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (c >= S) break;
+    const float wt = (l[c] == mx) ? 1.f : exp2_hw((l[c] - mx) * kLog2e);
+    den += wt;
+    num += wt * o[c];
+  }
+}
+
 __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   const long rh = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -469,15 +498,22 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int S = a.num_splits;
   const float* lp = a.lse_part + rh * S;
   const float* op = a.o_part + rh * S * kHeadDim + lane;
-  float mx = kNegInf;
-  for (int c = 0; c < S; ++c) mx = fmaxf(mx, lp[c]);
-  float den = 0.f, num = 0.f;
-  if (mx != kNegInf) {
-    for (int c = 0; c < S; ++c) {
-      const float l = lp[c];
-      const float wt = (l == mx) ? 1.f : exp2_hw((l - mx) * kLog2e);
-      den += wt;
-      num += wt * op[(long)c * kHeadDim];
+  float mx = kNegInf, den = 0.f, num = 0.f;
+  if (S <= 4) {
+    merge_regs<4>(lp, op, S, mx, den, num);
+  } else if (S <= 8) {
+    merge_regs<8>(lp, op, S, mx, den, num);
+  } else if (S <= 16) {
+    merge_regs<16>(lp, op, S, mx, den, num);
+  } else {
+    for (int c = 0; c < S; ++c) mx = fmaxf(mx, lp[c]);
+    if (mx != kNegInf) {
+      for (int c = 0; c < S; ++c) {
+        const float l = lp[c];
+        const float wt = (l == mx) ? 1.f : exp2_hw((l - mx) * kLog2e);
+        den += wt;
+        num += wt * op[(long)c * kHeadDim];
+      }
     }
   }
   const float o = den > 0.f ? num / den : 0.f;

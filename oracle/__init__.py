@@ -46,3 +46,4 @@ from .sink_attention import (  # noqa: F401
     attention_weights_ref,
     visible_range,
 )
+from .rope_append import append_rope_ref, append_positions, rotate  # noqa: F401

@@ -19,7 +19,9 @@ rotated dimensions, so:
 * R21 request b appends n_b tokens that take logical positions
       kv_len[b] - n_b .. kv_len[b] - 1 (kv_len counts them already, as the
       attention call that follows sees them); position p lives in page
-      page_indices[page_indptr[b] + p // 16], slot p % 16.
+      page_indices[page_indptr[b] + p // 16], slot p % 16.  A token whose
+      position lies outside the table ([0, max_pos)) has no angle: nothing of
+      it is written (its query row is left undefined, NaN here).
 """
 
 from __future__ import annotations
@@ -73,10 +75,15 @@ def append_rope_ref(q, k_new, v_new, append_indptr, kv_len, page_indptr, page_in
     qf, kf, vf = _as_f64(q), _as_f64(k_new), _as_f64(v_new)
     kp, vp = _as_f64(k_pool).copy(), _as_f64(v_pool).copy()
     req, pos = append_positions(append_indptr, kv_len)
-    q_out = rotate(qf, pos[:, None], cos_sin, interleaved)
-    k_rot = rotate(kf, pos[:, None], cos_sin, interleaved)
+    ok = (pos >= 0) & (pos < np.asarray(cos_sin).shape[0])
+    safe = np.where(ok, pos, 0)
+    q_out = rotate(qf, safe[:, None], cos_sin, interleaved)
+    q_out[~ok] = np.nan
+    k_rot = rotate(kf, safe[:, None], cos_sin, interleaved)
     page_size = kp.shape[2]
     for t, (b, p) in enumerate(zip(req, pos)):
+        if not ok[t]:
+            continue
         page = int(np.asarray(page_indices)[int(page_indptr[b]) + p // page_size])
         kp[page, :, p % page_size, :] = k_rot[t]
         vp[page, :, p % page_size, :] = vf[t]

@@ -53,7 +53,7 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="paged_decode",
                    choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
-                            "verify_decode", "verify_tree", "copy_calibration"],
+                            "verify_decode", "verify_tree", "append_rope", "copy_calibration"],
                    help="for profiling runs: time only this workload (copy_calibration: a plain "
                         "256 MiB device copy, the reference for HBM byte counters)")
     return p.parse_args()
@@ -238,6 +238,46 @@ def time_verify(w, args, torch, dev):
     return dict(step_ms=wall * 1e3, decode_ms=e0.elapsed_time(e1) / args.steps, splits=s)
 
 
+def time_append(args, torch, dev):
+    """Paged KV append with rotary embedding of queries and keys
+    (sinkattn_append_paged_kv_rope): 16 prefill chunks of 512 tokens on
+    prefixes uniform in [0, 16384], 64 query / 8 KV heads, random pages."""
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(0)
+    kv_len = (rng.integers(0, 16385, size=16) + 512).astype(np.int32)
+    n_new = np.full(16, 512, dtype=np.int32)
+    hq, hkv = 64, 8
+    append_indptr = np.concatenate([[0], np.cumsum(n_new)]).astype(np.int32)
+    n_pages = (kv_len + 15) // 16
+    page_indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    pool = int(page_indptr[-1])
+    page_indices = rng.permutation(pool).astype(np.int32)
+    t = int(append_indptr[-1])
+    bits = lambda shape: torch.from_numpy(wl._normal_bf16(rng, shape).view(np.int16)).to(dev).view(torch.bfloat16)
+    i32 = lambda a: torch.from_numpy(a).to(dev)
+    q, k, v = bits((t, hq, 64)), bits((t, hkv, 64)), bits((t, hkv, 64))
+    kp, vp = bits((pool, hkv, 16, 64)), bits((pool, hkv, 16, 64))
+    f = np.arange(32)
+    ang = np.arange(int(kv_len.max()) + 1)[:, None] * 10000.0 ** (-2.0 * f / 64)[None, :]
+    table = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to(dev)
+    q_out = torch.empty_like(q)
+    args_ = (k, v, i32(append_indptr), kp, vp, i32(page_indptr), i32(page_indices), i32(kv_len), table)
+    for _ in range(args.warmup):
+        sa.append_paged_kv_rope(*args_, q=q, q_out=q_out)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        sa.append_paged_kv_rope(*args_, q=q, q_out=q_out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = t * (2 * hq * 128 + 4 * hkv * 128 + 256) + 4 * (len(page_indices) + 3 * 17)
+    return dict(tokens=t, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
+
+
 def time_prefill(w, steps, warmup, torch, dev, window=0):
     from gqa_attention_sinks_amd import binding
     d = Dev(w, torch, dev)
@@ -404,6 +444,10 @@ def profile_only(args, torch, dev, wl):
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
                           "ms": dt * 1e3, "GBs_rw": 2 * n / dt / 1e9}))
+        return
+    if args.workload == "append_rope":
+        r = time_append(args, torch, dev)
+        print(json.dumps({"workload": "append_rope", **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
         return
     w = getattr(wl, args.workload)()
     log(f"timing {args.workload}")

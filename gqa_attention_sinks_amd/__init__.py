@@ -11,6 +11,7 @@ from .binding import (  # noqa: F401
     EXPORTED,
     SinkAttnError,
     abi_version,
+    append_paged_kv_rope,
     decode_paged,
     decode_paged_multi,
     kv_descriptor,

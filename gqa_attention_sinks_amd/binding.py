@@ -25,6 +25,7 @@ EXPORTED = (
     "sinkattn_prefill",
     "sinkattn_decode_paged",
     "sinkattn_decode_paged_multi",
+    "sinkattn_append_paged_kv_rope",
     "sinkattn_merge",
     "sinkattn_split_bounds",
     "sinkattn_pick_num_splits",
@@ -78,6 +79,9 @@ def load_library():
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp,
                                                 vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged_multi.restype = i32
+    lib.sinkattn_append_paged_kv_rope.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, i32, vp, i32,
+                                                  i32, i32, i32, i32, vp]
+    lib.sinkattn_append_paged_kv_rope.restype = i32
     lib.sinkattn_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge.restype = i32
     lib.sinkattn_split_bounds.argtypes = [vp, i32, i32, i32, vp]
@@ -309,6 +313,43 @@ def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, 
     if not want_out:
         return o_part, lse_part
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def append_paged_kv_rope(k_new, v_new, append_indptr, k_pool, v_pool, page_indptr, page_indices, kv_len,
+                         cos_sin, interleaved: bool = False, q=None, q_out=None, stream=None):
+    """Append the new tokens' keys/values to the paged pools with rotary
+    embedding of the keys and, when ``q`` is given, of the queries
+    (``sinkattn_append_paged_kv_rope``).  ``cos_sin`` is [max_pos, 64] fp32;
+    returns ``q_out`` (allocated if not given; may be ``q`` itself) or None."""
+    torch = _torch()
+    _dev(k_new, "k_new", torch.bfloat16)
+    if k_new.dim() != 3 or k_new.shape[2] != HEAD_DIM:
+        raise ValueError("k_new must be [total_new, Hkv, 64]")
+    total_new, hkv, _ = k_new.shape
+    _dev(v_new, "v_new", torch.bfloat16, k_new.shape)
+    _dev(append_indptr, "append_indptr", torch.int32)
+    batch = append_indptr.numel() - 1
+    _dev(cos_sin, "cos_sin", torch.float32)
+    if cos_sin.dim() != 2 or cos_sin.shape[1] != HEAD_DIM:
+        raise ValueError("cos_sin must be [max_pos, 64]")
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    if k_pool.shape[1] != hkv:
+        raise ValueError("k_new and the pools disagree on the KV head count")
+    hq = hkv
+    if q is not None:
+        _dev(q, "q", torch.bfloat16)
+        if q.dim() != 3 or q.shape[0] != total_new or q.shape[2] != HEAD_DIM:
+            raise ValueError("q must be [total_new, Hq, 64]")
+        hq = q.shape[1]
+        if q_out is None:
+            q_out = torch.empty_like(q)
+        _dev(q_out, "q_out", torch.bfloat16, q.shape)
+    lib = load_library()
+    _check(lib.sinkattn_append_paged_kv_rope(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(append_indptr),
+                                             ctypes.byref(kvs), _ptr(cos_sin), cos_sin.shape[0],
+                                             int(bool(interleaved)), _ptr(q_out if q is not None else None),
+                                             batch, total_new, hq, hkv, HEAD_DIM, _stream(stream)))
+    return q_out
 
 
 def merge(o_part, lse_part, out=None, lse=None, return_lse: bool = False, stream=None):

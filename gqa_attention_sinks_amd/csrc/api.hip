@@ -3,6 +3,7 @@
 // are in include/sinkattn.h.
 
 #include <math.h>
+#include <stdint.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -263,6 +264,45 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
     if ((st = hip_status(sinkattn::launch_merge(m, s), "merge launch")) != SINKATTN_OK) return st;
   }
   return SINKATTN_OK;
+}
+
+sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, const void* v_new,
+                                              const int32_t* append_indptr, const sinkattn_kv* kv,
+                                              const float* cos_sin, int32_t max_pos,
+                                              int32_t interleaved, void* q_out, int32_t batch,
+                                              int32_t total_new, int32_t num_qo_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              void* stream) {
+  REQUIRE(k_new != nullptr && v_new != nullptr && append_indptr != nullptr && cos_sin != nullptr,
+          SINKATTN_ERR_INVALID_ARG, "k_new, v_new, append_indptr and cos_sin are required");
+  REQUIRE((q == nullptr) == (q_out == nullptr), SINKATTN_ERR_INVALID_ARG,
+          "q and q_out must be given together (or both NULL)");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, 1.0f, 0);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_kv(kv, true)) != SINKATTN_OK) return st;
+  REQUIRE(total_new >= 0, SINKATTN_ERR_INVALID_ARG, "total_new must be >= 0 (got %d)", total_new);
+  REQUIRE(max_pos >= 1, SINKATTN_ERR_INVALID_ARG, "max_pos must be >= 1 (got %d)", max_pos);
+  REQUIRE(interleaved == 0 || interleaved == 1, SINKATTN_ERR_INVALID_ARG, "interleaved must be 0 or 1");
+  REQUIRE(((uintptr_t)cos_sin & 15) == 0, SINKATTN_ERR_INVALID_ARG, "cos_sin must be 16-byte aligned");
+  sinkattn::AppendArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k_new = static_cast<const uint16_t*>(k_new);
+  a.v_new = static_cast<const uint16_t*>(v_new);
+  a.append_indptr = append_indptr;
+  a.kv_len = kv->kv_len;
+  a.page_indptr = kv->kv_indptr;
+  a.page_indices = kv->page_indices;
+  a.cos_sin = cos_sin;
+  a.q_out = static_cast<uint16_t*>(q_out);
+  a.k_pool = static_cast<uint16_t*>(const_cast<void*>(kv->k));
+  a.v_pool = static_cast<uint16_t*>(const_cast<void*>(kv->v));
+  a.batch = batch;
+  a.total_new = total_new;
+  a.num_qo_heads = num_qo_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.max_pos = max_pos;
+  a.interleaved = interleaved;
+  return hip_status(sinkattn::launch_append_rope(a, static_cast<hipStream_t>(stream)), "append launch");
 }
 
 sinkattn_status sinkattn_merge(const float* o_part, const float* lse_part, int32_t rows,

@@ -60,7 +60,25 @@ struct PrefillArgs {
   int32_t num_slots;          // tile slots launched (upper bound on tiles)
 };
 
+// Paged KV append with rotary embedding of the new queries and keys; see
+// sinkattn_append_paged_kv_rope in include/sinkattn.h.
+struct AppendArgs {
+  const uint16_t* q;          // optional [T, Hq, 64] bf16 (null: keys only)
+  const uint16_t* k_new;      // [T, Hkv, 64] bf16
+  const uint16_t* v_new;      // [T, Hkv, 64] bf16
+  const int32_t* append_indptr;  // [B+1]
+  const int32_t* kv_len;      // [B], counting the appended tokens
+  const int32_t* page_indptr; // [B+1]
+  const int32_t* page_indices;
+  const float* cos_sin;       // [max_pos, 64]: cos of pair f in column f, sin in 32 + f
+  uint16_t* q_out;            // [T, Hq, 64] bf16 (may be q)
+  uint16_t* k_pool;           // [num_pages, Hkv, 16, 64]
+  uint16_t* v_pool;
+  int32_t batch, total_new, num_qo_heads, num_kv_heads, max_pos, interleaved;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_append_rope(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream);
 

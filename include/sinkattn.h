@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 3
+#define SINKATTN_ABI_VERSION 4
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
@@ -195,6 +195,39 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
                                             int32_t num_qo_heads, int32_t num_kv_heads,
                                             int32_t head_dim, float sm_scale, int32_t window,
                                             void* stream);
+
+/* Append new tokens' keys and values to a paged KV cache, with rotary
+ * position embedding applied to the new keys and (optionally) the new queries:
+ * the step just upstream of attention for a decode or verify batch.  "GPT-OSS
+ * on day 0", section "GPT-OSS on Hopper" (the models use YaRN rotary position
+ * encoding); "Accelerating Sonar through speculation", section "Inference
+ * with speculative decoding" (per-request pages, CPU-built page tables).  The
+ * pages give neither YaRN's constants nor the pair layout, so the rotation
+ * comes from the caller's table and layout flag:
+ *   pair f (0..31) is (x[f], x[f + 32]) (interleaved = 0) or (x[2f], x[2f + 1])
+ *   (interleaved = 1); at position p it becomes
+ *   (a cos - b sin, b cos + a sin) with cos = cos_sin[p][f], sin = cos_sin[p][32 + f].
+ * Request b appends n_b = append_indptr[b+1] - append_indptr[b] tokens, which
+ * take positions kv_len[b] - n_b .. kv_len[b] - 1 (kv_len already counts them,
+ * as the attention call that follows does); position p lives in page
+ * page_indices[kv_indptr[b] + p / 16], slot p % 16.
+ *   q        optional [total_new, Hq, 64] bf16 (NULL: keys only)
+ *   k_new, v_new [total_new, Hkv, 64] bf16
+ *   append_indptr [batch+1] int32 (device)
+ *   kv       paged descriptor (kv->paged must be 1); its pools are written at
+ *            the new tokens' slots only
+ *   cos_sin  [max_pos, 64] fp32 (device, 16-byte aligned)
+ *   q_out    [total_q, Hq, 64] bf16, written (may equal q); NULL when q is NULL
+ * Results are rounded to bf16 from fp32 arithmetic; values are copied
+ * exactly.  A token whose position falls outside [0, max_pos) is not written
+ * (its query row either).  Two appends that hit the same slot race. */
+sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, const void* v_new,
+                                              const int32_t* append_indptr, const sinkattn_kv* kv,
+                                              const float* cos_sin, int32_t max_pos,
+                                              int32_t interleaved, void* q_out, int32_t batch,
+                                              int32_t total_new, int32_t num_qo_heads,
+                                              int32_t num_kv_heads, int32_t head_dim,
+                                              void* stream);
 
 /* Log-sum-exp merge of split partials (the combination implied by splitting
  * the softmax along the KV sequence): per (row, head), with M = max_c lse_c

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 3
+    assert sa.abi_version() == 4
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -177,6 +177,35 @@ def test_decode_multi_argument_errors(lib, kwargs, code):
 
 def test_decode_multi_needs_paged(lib):
     assert _decode_multi(lib, _kv(paged=0)) == INVALID
+
+
+def _append(lib, kv, q=None, k=FAKE, v=FAKE, ai=FAKE, cs=FAKE, max_pos=128, inter=0, q_out=None, batch=2,
+            total=4, hq=8, hkv=2, d=64):
+    return lib.sinkattn_append_paged_kv_rope(q, k, v, ai, ctypes.byref(kv) if kv is not None else None, cs,
+                                             max_pos, inter, q_out, batch, total, hq, hkv, d, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(k=None), INVALID),
+    (dict(v=None), INVALID),
+    (dict(ai=None), INVALID),
+    (dict(cs=None), INVALID),
+    (dict(q=FAKE), INVALID),                       # q without q_out
+    (dict(q_out=FAKE), INVALID),                   # q_out without q
+    (dict(max_pos=0), INVALID),
+    (dict(inter=2), INVALID),
+    (dict(total=-1), INVALID),
+    (dict(d=128), UNSUPPORTED),
+    (dict(cs=ctypes.c_void_p(0x1004)), INVALID),   # table not 16-byte aligned
+    (dict(batch=0), INVALID),
+])
+def test_append_argument_errors(lib, kwargs, code):
+    assert _append(lib, _kv(), **kwargs) == code
+    assert lib.sinkattn_last_error()
+
+
+def test_append_needs_paged(lib):
+    assert _append(lib, _kv(paged=0)) == INVALID
 
 
 def test_merge_argument_errors(lib):

@@ -47,3 +47,4 @@ from .sink_attention import (  # noqa: F401
     visible_range,
 )
 from .rope_append import append_rope_ref, append_positions, rotate  # noqa: F401
+from .moe_routing import topk_softmax_ref  # noqa: F401

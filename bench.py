@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--workload", default="paged_decode",
                    choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
-                            "verify_decode", "verify_tree", "append_rope", "copy_calibration"],
+                            "verify_decode", "verify_tree", "append_rope", "moe_topk",
+                            "copy_calibration"],
                    help="for profiling runs: time only this workload (copy_calibration: a plain "
                         "256 MiB device copy, the reference for HBM byte counters)")
     return p.parse_args()
@@ -278,6 +279,31 @@ def time_append(args, torch, dev):
     return dict(tokens=t, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
 
 
+def time_moe(args, torch, dev):
+    """MoE routing weights (sinkattn_moe_topk_softmax): 65536 tokens of bf16
+    router logits N(0, 1), 128 experts, top 4."""
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import workloads as wl
+    t, e, k = 65536, 128, 4
+    logits = torch.from_numpy(wl._normal_bf16(np.random.default_rng(0), (t, e)).view(np.int16)).to(dev)
+    logits = logits.view(torch.bfloat16)
+    idx = torch.empty((t, k), dtype=torch.int32, device=dev)
+    w = torch.empty((t, k), dtype=torch.bfloat16, device=dev)
+    for _ in range(args.warmup):
+        sa.moe_topk_softmax(logits, k, idx, w)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        sa.moe_topk_softmax(logits, k, idx, w)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    nbytes = t * (e * 2 + k * 6)
+    return dict(tokens=t, experts=e, top_k=k, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
+
+
 def time_prefill(w, steps, warmup, torch, dev, window=0):
     from gqa_attention_sinks_amd import binding
     d = Dev(w, torch, dev)
@@ -444,6 +470,10 @@ def profile_only(args, torch, dev, wl):
         dt = (time.perf_counter() - t0) / args.steps
         print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
                           "ms": dt * 1e3, "GBs_rw": 2 * n / dt / 1e9}))
+        return
+    if args.workload == "moe_topk":
+        r = time_moe(args, torch, dev)
+        print(json.dumps({"workload": "moe_topk", **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
         return
     if args.workload == "append_rope":
         r = time_append(args, torch, dev)

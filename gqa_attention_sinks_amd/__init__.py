@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     library_path,
     load_library,
     merge,
+    moe_topk_softmax,
     pick_num_splits,
     prefill,
     split_bounds,

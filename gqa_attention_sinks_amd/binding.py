@@ -21,11 +21,14 @@ HEAD_DIM = 64
 PAGE_SIZE = 16
 MAX_SPLITS = 256
 MAX_DECODE_ROWS = 8
+MAX_EXPERTS = 512
+MAX_TOP_K = 8
 EXPORTED = (
     "sinkattn_prefill",
     "sinkattn_decode_paged",
     "sinkattn_decode_paged_multi",
     "sinkattn_append_paged_kv_rope",
+    "sinkattn_moe_topk_softmax",
     "sinkattn_merge",
     "sinkattn_split_bounds",
     "sinkattn_pick_num_splits",
@@ -82,6 +85,8 @@ def load_library():
     lib.sinkattn_append_paged_kv_rope.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, i32, vp, i32,
                                                   i32, i32, i32, i32, vp]
     lib.sinkattn_append_paged_kv_rope.restype = i32
+    lib.sinkattn_moe_topk_softmax.argtypes = [vp, i32, i32, i32, vp, vp, vp]
+    lib.sinkattn_moe_topk_softmax.restype = i32
     lib.sinkattn_merge.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp]
     lib.sinkattn_merge.restype = i32
     lib.sinkattn_split_bounds.argtypes = [vp, i32, i32, i32, vp]
@@ -350,6 +355,27 @@ def append_paged_kv_rope(k_new, v_new, append_indptr, k_pool, v_pool, page_indpt
                                              int(bool(interleaved)), _ptr(q_out if q is not None else None),
                                              batch, total_new, hq, hkv, HEAD_DIM, _stream(stream)))
     return q_out
+
+
+def moe_topk_softmax(logits, top_k: int, topk_idx=None, topk_w=None, stream=None):
+    """Top-K experts per token and the softmax over their logits alone
+    (``sinkattn_moe_topk_softmax``): ``logits`` [T, E] bf16 -> (``topk_idx``
+    [T, K] int32, ``topk_w`` [T, K] bf16)."""
+    torch = _torch()
+    _dev(logits, "logits", torch.bfloat16)
+    if logits.dim() != 2:
+        raise ValueError("logits must be [num_tokens, num_experts]")
+    t, e = logits.shape
+    k = int(top_k)
+    if topk_idx is None:
+        topk_idx = torch.empty((t, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((t, k), dtype=torch.bfloat16, device=logits.device)
+    _dev(topk_idx, "topk_idx", torch.int32, (t, k))
+    _dev(topk_w, "topk_w", torch.bfloat16, (t, k))
+    lib = load_library()
+    _check(lib.sinkattn_moe_topk_softmax(_ptr(logits), t, e, k, _ptr(topk_idx), _ptr(topk_w), _stream(stream)))
+    return topk_idx, topk_w
 
 
 def merge(o_part, lse_part, out=None, lse=None, return_lse: bool = False, stream=None):

@@ -305,6 +305,20 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
   return hip_status(sinkattn::launch_append_rope(a, static_cast<hipStream_t>(stream)), "append launch");
 }
 
+sinkattn_status sinkattn_moe_topk_softmax(const void* logits, int32_t num_tokens, int32_t num_experts,
+                                          int32_t top_k, int32_t* topk_idx, void* topk_w, void* stream) {
+  REQUIRE(logits != nullptr && topk_idx != nullptr && topk_w != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "logits, topk_idx and topk_w are required");
+  REQUIRE(num_tokens >= 0, SINKATTN_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
+  REQUIRE(num_experts >= 1 && num_experts <= SINKATTN_MAX_EXPERTS, SINKATTN_ERR_UNSUPPORTED,
+          "num_experts must be in [1, %d] (got %d)", SINKATTN_MAX_EXPERTS, num_experts);
+  REQUIRE(top_k >= 1 && top_k <= SINKATTN_MAX_TOP_K && top_k <= num_experts, SINKATTN_ERR_INVALID_ARG,
+          "top_k must be in [1, min(%d, num_experts)] (got %d)", SINKATTN_MAX_TOP_K, top_k);
+  sinkattn::MoeArgs a{static_cast<const uint16_t*>(logits), topk_idx, static_cast<uint16_t*>(topk_w),
+                      num_tokens, num_experts, top_k};
+  return hip_status(sinkattn::launch_moe_topk_softmax(a, static_cast<hipStream_t>(stream)), "moe launch");
+}
+
 sinkattn_status sinkattn_merge(const float* o_part, const float* lse_part, int32_t rows,
                                int32_t num_heads, int32_t num_splits, int32_t head_dim, void* out,
                                float* lse_out, void* stream) {

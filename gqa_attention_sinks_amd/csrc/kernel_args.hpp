@@ -77,7 +77,16 @@ struct AppendArgs {
   int32_t batch, total_new, num_qo_heads, num_kv_heads, max_pos, interleaved;
 };
 
+// MoE routing weights; see sinkattn_moe_topk_softmax in include/sinkattn.h.
+struct MoeArgs {
+  const uint16_t* logits;     // [T, E] bf16
+  int32_t* topk_idx;          // [T, K]
+  uint16_t* topk_w;           // [T, K] bf16
+  int32_t num_tokens, num_experts, top_k;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream);
 hipError_t launch_append_rope(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream);

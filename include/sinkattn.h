@@ -57,11 +57,13 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 4
+#define SINKATTN_ABI_VERSION 5
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
 #define SINKATTN_MAX_DECODE_ROWS 8
+#define SINKATTN_MAX_EXPERTS 512
+#define SINKATTN_MAX_TOP_K 8
 
 typedef enum {
   SINKATTN_OK = 0,
@@ -228,6 +230,23 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
                                               int32_t total_new, int32_t num_qo_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               void* stream);
+
+/* MoE routing weights of GPT-OSS: for every token the top_k largest router
+ * logits and the softmax over those top_k logits alone ("GPT-OSS on day 0",
+ * sections "GPT-OSS on Hopper" and "Kernels for GPT-OSS > MoE": softmax after
+ * the top-K selection, over the selected experts only, with the expert
+ * weights computed in bfloat16 precision).  The selection compares the bf16
+ * logits exactly; equal logits (-0 equals +0) rank the lower expert index
+ * first.  The softmax runs in fp32 on the bf16 logits and is rounded to bf16.
+ *   logits    [num_tokens, num_experts] bf16 (device); NaN logits give
+ *             unspecified picks
+ *   topk_idx  [num_tokens, top_k] int32, written: expert ids, largest logit
+ *             first
+ *   topk_w    [num_tokens, top_k] bf16, written: the weights, same order
+ *   1 <= num_experts <= SINKATTN_MAX_EXPERTS, 1 <= top_k <=
+ *   min(SINKATTN_MAX_TOP_K, num_experts). */
+sinkattn_status sinkattn_moe_topk_softmax(const void* logits, int32_t num_tokens, int32_t num_experts,
+                                          int32_t top_k, int32_t* topk_idx, void* topk_w, void* stream);
 
 /* Log-sum-exp merge of split partials (the combination implied by splitting
  * the softmax along the KV sequence): per (row, head), with M = max_c lse_c

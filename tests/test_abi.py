@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 4
+    assert sa.abi_version() == 5
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -206,6 +206,21 @@ def test_append_argument_errors(lib, kwargs, code):
 
 def test_append_needs_paged(lib):
     assert _append(lib, _kv(paged=0)) == INVALID
+
+
+@pytest.mark.parametrize("args,code", [
+    ((None, 4, 32, 4, FAKE, FAKE), INVALID),
+    ((FAKE, 4, 32, 4, None, FAKE), INVALID),
+    ((FAKE, 4, 32, 4, FAKE, None), INVALID),
+    ((FAKE, -1, 32, 4, FAKE, FAKE), INVALID),
+    ((FAKE, 4, 0, 1, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, 4, 513, 4, FAKE, FAKE), UNSUPPORTED),
+    ((FAKE, 4, 32, 0, FAKE, FAKE), INVALID),
+    ((FAKE, 4, 32, 9, FAKE, FAKE), INVALID),
+    ((FAKE, 4, 3, 4, FAKE, FAKE), INVALID),
+])
+def test_moe_argument_errors(lib, args, code):
+    assert lib.sinkattn_moe_topk_softmax(*args, None) == code
 
 
 def test_merge_argument_errors(lib):

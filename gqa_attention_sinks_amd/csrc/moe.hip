@@ -7,21 +7,23 @@
 // all experts as DeepSeek-style models do, and the expert weights must be
 // computed in bfloat16 precision).
 //
-// One wave per token.  Each logit becomes a 32-bit key: the bf16 bits mapped
-// to an unsigned order (larger logit, larger key) in the high half and the
-// complemented expert index in the low half, so one unsigned max picks the
-// largest logit and, among equal logits, the lowest index.  K rounds of a
-// wave-wide max (six xor exchanges) select the experts in order; the selected
-// key is then cleared.  The softmax over the K selected bf16 logits runs in
-// fp32 and is rounded to bf16.
+// Eight lanes per token (eight tokens per wave).  Each logit becomes a
+// 32-bit key: the bf16 bits mapped to an unsigned order (larger logit, larger
+// key) in the high half and the complemented expert index in the low half, so
+// one unsigned comparison orders by logit and, among equal logits, puts the
+// lower index first.  Each lane keeps the top KP keys of its own experts in a
+// descending register list (an insertion per key); three exchange levels
+// (lanes 1, 2, 4 apart) merge the eight lists: the elementwise max of a list
+// and its partner's reversed list holds the top KP of both, and a bitonic
+// network sorts it.  Every lane then holds the token's top KP; lane s < K
+// writes the s-th expert and its weight, the softmax over the K selected bf16
+// logits evaluated in fp32 and rounded to bf16.
 
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
 namespace sinkattn {
 namespace {
-
-constexpr int kMoeMaxPerLane = 8;   // experts per lane: up to 512 experts
 
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
   const int src = __lane_id() ^ mask;
@@ -35,52 +37,107 @@ __device__ __forceinline__ uint32_t order_key(uint16_t bits, int expert) {
   return (ord << 16) | (uint32_t)(0xffff - expert);
 }
 
+// the logit of a key (inverse of the order map), as fp32
+__device__ __forceinline__ float key_logit(uint32_t key) {
+  const uint32_t ord = key >> 16;
+  const uint32_t bits = (ord & 0x8000u) ? (ord ^ 0x8000u) : (~ord & 0xffffu);
+  return __builtin_bit_cast(float, bits << 16);
+}
+
+template <int KP>
+__device__ __forceinline__ void sort_bitonic_desc(uint32_t (&m)[KP]) {
+#pragma unroll
+  for (int d = KP / 2; d >= 1; d /= 2)
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+      if ((i & d) == 0) {
+        const uint32_t hi = max(m[i], m[i + d]), lo = min(m[i], m[i + d]);
+        m[i] = hi;
+        m[i + d] = lo;
+      }
+}
+
+template <int KP>
 __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
-  const long t = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= a.num_tokens) return;                 // uniform per wave
-  const uint16_t* row = a.logits + t * a.num_experts;
-  uint32_t key[kMoeMaxPerLane];
+  const int s = lane & 7;                                    // this lane's share of the experts
+  const long t = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+  const bool live = t < a.num_tokens;
+  const int per = (a.num_experts + 7) / 8;
+  const int e0 = s * per, e1 = min(e0 + per, a.num_experts);
+
+  uint32_t top[KP];                                          // descending; 0 is below every key
 #pragma unroll
-  for (int i = 0; i < kMoeMaxPerLane; ++i) {
-    const int e = i * 64 + lane;
-    key[i] = e < a.num_experts ? order_key(row[e], e) : 0u;   // 0: below every real key
-  }
-  float sel_logit = 0.f;   // lane r < K keeps the r-th selected logit
-  int sel_idx = 0;
-  for (int r = 0; r < a.top_k; ++r) {
-    uint32_t best = 0u;
+  for (int i = 0; i < KP; ++i) top[i] = 0u;
+  auto insert = [&](uint32_t key) {
 #pragma unroll
-    for (int i = 0; i < kMoeMaxPerLane; ++i) best = max(best, key[i]);
+    for (int i = 0; i < KP; ++i) {                           // larger keys move up
+      const uint32_t hi = max(top[i], key);
+      key = min(top[i], key);
+      top[i] = hi;
+    }
+  };
+  if (live) {
+    const uint16_t* row = a.logits + t * a.num_experts;
+    if (a.num_experts % 64 == 0) {
+      // whole 16-byte chunks (8 logits) per lane, all loads issued first
+      const int nch = per / 8;                               // 1 .. 8
+      u32x4 ch[8];
 #pragma unroll
-    for (int m = 32; m > 0; m >>= 1) best = max(best, shfl_xor_u32(best, m));
-    const int e = 0xffff - (int)(best & 0xffffu);
-    // clear the winner (its key is unique: the index is in it)
+      for (int c = 0; c < 8; ++c)
+        if (c < nch) ch[c] = *reinterpret_cast<const u32x4*>(row + e0 + 8 * c);
 #pragma unroll
-    for (int i = 0; i < kMoeMaxPerLane; ++i)
-      if (key[i] == best) key[i] = 0u;
-    if (lane == r) {
-      sel_idx = e;
-      sel_logit = __builtin_bit_cast(float, (uint32_t)row[e] << 16);
+      for (int c = 0; c < 8; ++c) {
+        if (c >= nch) break;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          insert(order_key((uint16_t)(ch[c][w] & 0xffffu), e0 + 8 * c + 2 * w));
+          insert(order_key((uint16_t)(ch[c][w] >> 16), e0 + 8 * c + 2 * w + 1));
+        }
+      }
+    } else {
+      for (int e = e0; e < e1; ++e) insert(order_key(row[e], e));
     }
   }
-  // softmax over the selected logits (lanes 0 .. K-1); the first is the largest
-  const float top = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, sel_logit)));
-  float ex = lane < a.top_k ? exp2_hw((sel_logit - top) * kLog2e) : 0.f;
-  float sum = ex;
+  // merge the eight lists of the token's lanes (every lane takes part: the
+  // exchanges stay inside each 8-lane group)
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) sum += shfl_xor_f32(sum, m);   // K <= 8: lanes 0..7 hold every term
-  if (lane < a.top_k) {
-    a.topk_idx[t * a.top_k + lane] = sel_idx;
-    a.topk_w[t * a.top_k + lane] = to_bf16_bits(ex / sum);
+  for (int m = 1; m < 8; m <<= 1) {
+    uint32_t other[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) other[i] = shfl_xor_u32(top[i], m);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) top[i] = max(top[i], other[KP - 1 - i]);
+    sort_bitonic_desc<KP>(top);
   }
+  if (!live || s >= a.top_k) return;
+  // softmax over the K selected logits (each lane sums them itself)
+  const float l0 = key_logit(top[0]);
+  float sum = 0.f, mine = 0.f;
+  uint32_t my_key = top[0];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (i >= a.top_k) break;
+    const float ex = exp2_hw((key_logit(top[i]) - l0) * kLog2e);
+    sum += ex;
+    if (i == s) {
+      mine = ex;
+      my_key = top[i];
+    }
+  }
+  a.topk_idx[t * a.top_k + s] = 0xffff - (int)(my_key & 0xffffu);
+  a.topk_w[t * a.top_k + s] = to_bf16_bits(mine / sum);
 }
 
 }  // namespace
 
 hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream) {
   if (a.num_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(moe_topk_softmax_kernel, dim3((unsigned)((a.num_tokens + 3) / 4)), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)((a.num_tokens + 31) / 32)), block(256);   // 32 tokens per workgroup
+  if (a.top_k <= 1) hipLaunchKernelGGL(moe_topk_softmax_kernel<1>, grid, block, 0, stream, a);
+  else if (a.top_k <= 2) hipLaunchKernelGGL(moe_topk_softmax_kernel<2>, grid, block, 0, stream, a);
+  else if (a.top_k <= 4) hipLaunchKernelGGL(moe_topk_softmax_kernel<4>, grid, block, 0, stream, a);
+  else hipLaunchKernelGGL(moe_topk_softmax_kernel<8>, grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -517,27 +517,29 @@ void prefill_kernel(PrefillArgs a) {
       f32x16 s0[2], s1[2];
       f16x8 p0[2][2], p1[2][2];
       float t0s[2], t1s[2];
-      {
-        bf16x8 kop[4];
-        read_k(0, kop);
-        mma_scores(kop, s0);
-        reads_then_mfmas<4, 8>();
-      }
+      // Every step's LDS operands are read one step ahead: both K halves
+      // before S0, V0 at the start of S1's step, V1 at the start of P0.V0's,
+      // so no step waits on its own reads.
+      bf16x8 k0[4], k1[4];
+      read_k(0, k0);
+      read_k(1, k1);
+      mma_scores(k0, s0);
+      reads_then_mfmas<8, 8>();
       if (need_mask) mask_half(0, s0);
       // The two overlapped steps are interleaved by hand: each MFMA is
       // followed by four weights of the other half (fma, exp2, pack), and
       // scheduling fences keep the compiler from regrouping them, so the
       // wave issues vector work while its matrix product runs.
+      f16x8 v0[2][2];
+      read_v(0, v0);
       {
-        bf16x8 kop[4];
-        read_k(1, kop);
         f16x2 h[2][8];
         s1[0] = f32x16{};
         s1[1] = f32x16{};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int kstep = u >> 1, rb = u & 1;
-          s1[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[kstep], qop[rb][kstep], s1[rb], 0, 0, 0);
+          s1[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1[kstep], qop[rb][kstep], s1[rb], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           weight_pair(s0, m, c, u >> 2, 2 * (u & 3), h);
           weight_pair(s0, m, c, u >> 2, 2 * (u & 3) + 1, h);
@@ -549,14 +551,14 @@ void prefill_kernel(PrefillArgs a) {
       dsum[0] += t0s[0];
       dsum[1] += t0s[1];
       if (need_mask) mask_half(1, s1);
+      f16x8 v1[2][2];
+      read_v(1, v1);
       {
-        f16x8 vt[2][2];
-        read_v(0, vt);
         f16x2 h[2][8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int hh = u >> 2, db = (u >> 1) & 1, rb = u & 1;
-          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[hh][db], p0[rb][hh], acc[rb][db], 0, 0, 0);
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v0[hh][db], p0[rb][hh], acc[rb][db], 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           weight_pair(s1, m, c, u >> 2, 2 * (u & 3), h);
           weight_pair(s1, m, c, u >> 2, 2 * (u & 3) + 1, h);
@@ -567,12 +569,7 @@ void prefill_kernel(PrefillArgs a) {
       if (__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit || t1s[1] > kSumLimit) != 0) rebase(1, p1, t1s);
       dsum[0] += t1s[0];
       dsum[1] += t1s[1];
-      {
-        f16x8 vt[2][2];
-        read_v(1, vt);
-        mma_pv(vt, p1);
-        reads_then_mfmas<8, 8>();
-      }
+      mma_pv(v1, p1);
     }
 
     if (more) store_tile(STAGE ^ 1, kt + kBN, kr, vr);

@@ -57,9 +57,13 @@ __device__ __forceinline__ int page_swizzle(int key, int chunk) {
 
 template <int NW, int NB>
 struct DecodeSmem {
+  // Several column blocks: Q operands staged once per workgroup (after the
+  // V staging area) and the waves merged one 16-column block at a time.
+  static constexpr bool kQInLds = NB >= 2;
   static constexpr int kStage = NW * kPageBytes;
-  static constexpr int kMerge = NW * 16 * NB * (kHeadDim + 2) * 4;
-  static constexpr int kBytes = kStage > kMerge ? kStage : kMerge;
+  static constexpr int kQ = kQInLds ? NB * 2 * 64 * 16 : 0;
+  static constexpr int kMerge = NW * 16 * (kQInLds ? 1 : NB) * (kHeadDim + 2) * 4;
+  static constexpr int kBytes = kStage + kQ > kMerge ? kStage + kQ : kMerge;
 };
 
 // Requests ranked by KV length (longest first), so that the longest chunks
@@ -186,25 +190,44 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
   // This lane's columns: Q^T operands of the score MFMA (column = (row, head),
   // k = dims 16*grp + 8*ks + e) and, with several rows, each column's own
   // visible key range [c_lo, c_pos].
-  bf16x8 q0[NB], q1[NB];
+  // With several column blocks the operands live in LDS (loaded once by
+  // wave 0, read per page), which keeps the register count at three waves
+  // per SIMD; one block stays in registers.
+  constexpr bool kQLds = DecodeSmem<NW, NB>::kQInLds;
+  constexpr int QR = kQLds ? 1 : NB;
+  bf16x8 q0[QR], q1[QR];
   int c_lo[NB], c_pos[NB];
   int c_bit[NB];   // MASK: bit offset of the column's mask row in the request's mask (-1: no row)
+  u32x4* const q_lds = reinterpret_cast<u32x4*>(smem + DecodeSmem<NW, NB>::kStage);   // [NB][2][64 lanes]
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
     const int j = 16 * nb + col;
     const int t = j / G;
     const int head = g * G + (j - t * G);
-    q0[nb] = bf16x8{};
-    q1[nb] = bf16x8{};
-    if (t < n_q) {
-      const uint16_t* qp = a.q + ((size_t)(qrow + t) * a.num_qo_heads + head) * kHeadDim + 16 * grp;
-      q0[nb] = __builtin_bit_cast(bf16x8, ldg16(qp));
-      q1[nb] = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
+    if (!kQLds || wave == 0) {
+      bf16x8 x0 = {}, x1 = {};
+      if (t < n_q) {
+        const uint16_t* qp = a.q + ((size_t)(qrow + t) * a.num_qo_heads + head) * kHeadDim + 16 * grp;
+        x0 = __builtin_bit_cast(bf16x8, ldg16(qp));
+        x1 = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
+      }
+      if (kQLds) {
+        q_lds[(nb * 2) * 64 + lane] = __builtin_bit_cast(u32x4, x0);
+        q_lds[(nb * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, x1);
+      } else {
+        q0[nb < QR ? nb : 0] = x0;
+        q1[nb < QR ? nb : 0] = x1;
+      }
     }
     c_pos[nb] = n_k - n_q + t;
     c_lo[nb] = a.window > 0 ? c_pos[nb] - a.window + 1 : 0;
     c_bit[nb] = t < n_q ? t * n_k : -1;
   }
+  if (kQLds) __syncthreads();
+  auto qop = [&](int nb, int half) -> bf16x8 {
+    if (kQLds) return __builtin_bit_cast(bf16x8, q_lds[(nb * 2 + half) * 64 + lane]);
+    return half ? q1[nb < QR ? nb : 0] : q0[nb < QR ? nb : 0];
+  };
   // the request's mask: row t, key j is bit t * n_k + j (little-endian bytes)
   const uint8_t* mbytes = MASK ? a.custom_mask + a.mask_indptr[b] : nullptr;
 
@@ -288,8 +311,8 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
       for (int nb = 0; nb < NB; ++nb) {
         sc[nb] = f32x4{};
         if (nb >= nb_used) continue;
-        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), q0[nb], sc[nb], 0, 0, 0);
-        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), q1[nb], sc[nb], 0, 0, 0);
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), qop(nb, 0), sc[nb], 0, 0, 0);
+        sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), qop(nb, 1), sc[nb], 0, 0, 0);
       }
       const u32x4 v0r = vc[u][0], v1r = vc[u][1];
       uint32_t mcur[NB];
@@ -409,54 +432,62 @@ __global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
     dsum[nb] += shfl_xor_f32(dsum[nb], 32);
   }
 
-  // merge the waves through LDS
-  constexpr int kCols = 16 * NB;
-  __syncthreads();
+  // merge the waves through LDS, kMB column blocks at a time
+  constexpr int kMB = kQLds ? 1 : NB;
+  constexpr int kCols = 16 * kMB;
   float* sm_m = reinterpret_cast<float*>(smem);
   float* sm_d = sm_m + NW * kCols;
   float* sm_o = sm_d + NW * kCols;   // [NW][kCols][64 dims]
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int j = 16 * nb + col;
-    if (grp == 0) {
-      sm_m[wave * kCols + j] = m[nb];
-      sm_d[wave * kCols + j] = dsum[nb];
-    }
+  for (int nb0 = 0; nb0 < NB; nb0 += kMB) {
+    if (nb0 >= nb_used) break;                       // uniform
+    __syncthreads();                                 // the staging area (or the last round) is free
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-      *reinterpret_cast<f32x4*>(sm_o + (wave * kCols + j) * kHeadDim + 16 * db + 4 * grp) = acc[nb][db];
-  }
-  __syncthreads();
+    for (int k = 0; k < kMB; ++k) {
+      const int nb = nb0 + k;
+      const int jl = 16 * k + col;
+      if (grp == 0) {
+        sm_m[wave * kCols + jl] = m[nb];
+        sm_d[wave * kCols + jl] = dsum[nb];
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+        *reinterpret_cast<f32x4*>(sm_o + (wave * kCols + jl) * kHeadDim + 16 * db + 4 * grp) = acc[nb][db];
+    }
+    __syncthreads();
 
-  for (int idx = threadIdx.x; idx < n_q * G * kHeadDim; idx += NW * 64) {
-    const int j = idx / kHeadDim;
-    const int d = idx % kHeadDim;
-    const int t = j / G;
-    const int h = g * G + (j - t * G);
-    // each wave's reference is finite (-FLT_MAX until its first visible key)
-    float mx = -kFloatMax;
+    const int ncols = min(kCols, n_q * G - 16 * nb0);   // real columns of these blocks
+    for (int idx = threadIdx.x; idx < ncols * kHeadDim; idx += NW * 64) {
+      const int jl = idx / kHeadDim;
+      const int d = idx % kHeadDim;
+      const int j = 16 * nb0 + jl;
+      const int t = j / G;
+      const int h = g * G + (j - t * G);
+      // each wave's reference is finite (-FLT_MAX until its first visible key)
+      float mx = -kFloatMax;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * kCols + j]);
-    float den = 0.f, num = 0.f;
+      for (int w = 0; w < NW; ++w) mx = fmaxf(mx, sm_m[w * kCols + jl]);
+      float den = 0.f, num = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = sm_m[w * kCols + j];
-      const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
-      den += wt * sm_d[w * kCols + j];
-      num += wt * sm_o[(w * kCols + j) * kHeadDim + d];
-    }
-    const float sink2 = (c == 0 && a.sinks != nullptr) ? a.sinks[h] * kLog2e : kNegInf;
-    float lse2;
-    // no visible key in the chunk: the key part is empty (d = 0)
-    const float o = num * fold_sink(sink2, den > 0.f ? mx : kNegInf, den, &lse2);
-    const float lse_nat = lse2 * kLn2;
-    const size_t rh = (size_t)(qrow + t) * a.num_qo_heads + h;
-    if (S == 1) {
-      a.out[rh * kHeadDim + d] = to_bf16_bits(o);
-      if (a.lse != nullptr && d == 0) a.lse[rh] = lse_nat;
-    } else {
-      a.o_part[(rh * S + c) * kHeadDim + d] = o;
-      if (d == 0) a.lse_part[rh * S + c] = lse_nat;
+      for (int w = 0; w < NW; ++w) {
+        const float mw = sm_m[w * kCols + jl];
+        const float wt = (mw == mx) ? 1.f : exp2_hw(mw - mx);
+        den += wt * sm_d[w * kCols + jl];
+        num += wt * sm_o[(w * kCols + jl) * kHeadDim + d];
+      }
+      const float sink2 = (c == 0 && a.sinks != nullptr) ? a.sinks[h] * kLog2e : kNegInf;
+      float lse2;
+      // no visible key in the chunk: the key part is empty (d = 0)
+      const float o = num * fold_sink(sink2, den > 0.f ? mx : kNegInf, den, &lse2);
+      const float lse_nat = lse2 * kLn2;
+      const size_t rh = (size_t)(qrow + t) * a.num_qo_heads + h;
+      if (S == 1) {
+        a.out[rh * kHeadDim + d] = to_bf16_bits(o);
+        if (a.lse != nullptr && d == 0) a.lse[rh] = lse_nat;
+      } else {
+        a.o_part[(rh * S + c) * kHeadDim + d] = o;
+        if (d == 0) a.lse_part[rh * S + c] = lse_nat;
+      }
     }
   }
 }

@@ -14,7 +14,7 @@
 #include "sinkattn.h"
 
 namespace sinkattn {
-int prefill_rows_per_tile(int32_t window);
+int prefill_rows_per_tile(int32_t window, int32_t group);
 }
 
 namespace {
@@ -86,7 +86,7 @@ sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const 
   REQUIRE(total_q >= batch, SINKATTN_ERR_INVALID_ARG, "total_q (%d) must be >= batch (%d): every request has a query row",
           total_q, batch);
 
-  const int bm = sinkattn::prefill_rows_per_tile(window);
+  const int bm = sinkattn::prefill_rows_per_tile(window, num_qo_heads / num_kv_heads);
   sinkattn::PrefillArgs a{};
   a.q = static_cast<const uint16_t*>(q);
   a.qo_indptr = qo_indptr;

@@ -6,9 +6,11 @@
 // starts from (sink, 1), so the sink costs nothing per key.
 //
 // Work decomposition (gfx950):
-//   workgroup = (tile of 256 query rows of one request, one query head);
-//   4 waves x 64 query rows (two 32-row MFMA blocks, so every K/V operand
-//   read from LDS feeds two MFMAs); two workgroups per CU, so each SIMD runs
+//   workgroup = 4 waves of 64 query rows each (two 32-row MFMA blocks, so
+//   every K/V operand read from LDS feeds two MFMAs): the same 64 rows of four
+//   query heads that share a KV head when the GQA group splits into fours
+//   (every wave then needs exactly the workgroup's key tiles), else 256
+//   consecutive rows of one head.  Two workgroups per CU, so each SIMD runs
 //   two waves whose matrix and vector phases overlap.  Consecutive workgroup
 //   ids walk the KV heads first, so with 8 KV heads and 8 XCDs each XCD's L2
 //   serves one KV head.  Tiles of a request are issued longest first (causal
@@ -46,7 +48,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 64;               // two 32-row MFMA blocks per wave
-constexpr int kBM = kWaves * kRowsPerWave;     // query rows per workgroup
 constexpr int kBN = 64;                        // keys per tile
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 8 KiB
 constexpr float kSumLimit = 16384.f;           // 2^14
@@ -118,11 +119,13 @@ __device__ __forceinline__ TileLanes tile_lanes(int lane) {
   return t;
 }
 
-// Key tiles a query tile spans (the work of a workgroup, in 64-key tiles).
+// Key tiles a query tile of RT rows spans (the work of a workgroup, in
+// 64-key tiles).
+template <int RT>
 __device__ __forceinline__ int tile_work(int n_q, int n_k, int t, int window) {
   const int shift = n_k - n_q;
-  const int t0 = t * kBM;
-  const int t_last = min(t0 + kBM, n_q) - 1;
+  const int t0 = t * RT;
+  const int t_last = min(t0 + RT, n_q) - 1;
   const int lo_first = window > 0 ? max(0, shift + t0 - window + 1) : 0;
   const int k_first = (lo_first / kBN) * kBN;
   return (shift + t_last + 1 - k_first + kBN - 1) / kBN;
@@ -136,6 +139,7 @@ __device__ __forceinline__ int tile_work(int n_q, int n_k, int t, int window) {
 // ones fill the tail.  Otherwise they take them request by request, longest
 // tile first: with equal requests that order is as balanced, and tiles of
 // one request that run together share its keys in L2.
+template <int RT>
 __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* out_b, int* out_tile) {
   constexpr int kThreads = kWaves * 64;
   const int tid = threadIdx.x;
@@ -144,7 +148,7 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   const int b1 = min(b0 + per, a.batch);
   auto req_tiles = [&](int b) {
     const int n = a.qo_indptr[b + 1] - a.qo_indptr[b];
-    return (a.skip_single_rows && n == 1) ? 0 : (n + kBM - 1) / kBM;
+    return (a.skip_single_rows && n == 1) ? 0 : (n + RT - 1) / RT;
   };
   auto req_len = [&](int b, int* n_q, int* n_k) {
     *n_q = a.qo_indptr[b + 1] - a.qo_indptr[b];
@@ -185,7 +189,7 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
       int n_q, n_k;
       req_len(b, &n_q, &n_k);
       for (int t = 0; t < nt; ++t, ++pos) {
-        s_work[pos] = tile_work(n_q, n_k, t, a.window);
+        s_work[pos] = tile_work<RT>(n_q, n_k, t, a.window);
         s_req[pos] = b;
         s_tile[pos] = t;
       }
@@ -267,9 +271,15 @@ __device__ __forceinline__ void half_weights(const f32x16 (&s)[2], const float (
   finish_weights(h, pop, tsum);
 }
 
-template <bool PAGED>
+// HP: query heads per workgroup.  HP = 1: the four waves take four 64-row
+// blocks of one head (256 rows a tile).  HP = 4: they take the same 64 rows
+// of four heads that share a KV head, so every wave needs exactly the
+// workgroup's key tiles (no wave waits out another's diagonal or window
+// edge).
+template <bool PAGED, int HP>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillArgs a) {
+  constexpr int RT = kRowsPerWave * (kWaves / HP);   // query rows of a workgroup tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
   __shared__ int s_scan[kWaves * 64];
 
@@ -282,12 +292,13 @@ void prefill_kernel(PrefillArgs a) {
   int id = blockIdx.x;
   const int g = id % a.num_kv_heads;
   id /= a.num_kv_heads;
-  const int hg = id % a.group;
-  const int slot = id / a.group;
-  const int head = g * a.group + hg;
+  const int hgroups = a.group / HP;                 // head groups of one KV head
+  const int hg = id % hgroups;
+  const int slot = id / hgroups;
+  const int head = g * a.group + hg * HP + (HP > 1 ? wave : 0);   // this wave's query head
 
   int b, tile;
-  if (!locate_tile(a, slot, s_scan, &b, &tile)) return;   // uniform over the workgroup
+  if (!locate_tile<RT>(a, slot, s_scan, &b, &tile)) return;   // uniform over the workgroup
   b = __builtin_amdgcn_readfirstlane(b);
   tile = __builtin_amdgcn_readfirstlane(tile);
 
@@ -301,8 +312,8 @@ void prefill_kernel(PrefillArgs a) {
     n_k = a.kv_indptr[b + 1] - kv_begin;
   }
   const int shift = n_k - n_q;   // row t sits at key position shift + t
-  const int t0 = tile * kBM;
-  const int t_last = min(t0 + kBM, n_q) - 1;
+  const int t0 = tile * RT;
+  const int t_last = min(t0 + RT, n_q) - 1;
   const int W = a.window;
   const int lo_first = W > 0 ? max(0, shift + t0 - W + 1) : 0;
   const int k_first = (lo_first / kBN) * kBN;
@@ -310,7 +321,7 @@ void prefill_kernel(PrefillArgs a) {
   const int ntiles = (k_end - k_first + kBN - 1) / kBN;
 
   // this wave's 64 rows (two 32-row MFMA blocks) and the two rows of this lane
-  const int wt0 = t0 + kRowsPerWave * wave;
+  const int wt0 = t0 + (HP > 1 ? 0 : kRowsPerWave * wave);
   const bool wave_live = wt0 <= t_last;
   const int wp_min = shift + wt0;
   const int wp_max = shift + min(wt0 + kRowsPerWave - 1, t_last);
@@ -607,20 +618,28 @@ void prefill_kernel(PrefillArgs a) {
 
 }  // namespace
 
+// Heads per workgroup: four when the GQA group splits into fours, else one.
+static int heads_per_workgroup(int32_t group) { return group % 4 == 0 ? 4 : 1; }
+
 hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream) {
   (void)total_q;
-  const long blocks = (long)a.num_slots * a.num_qo_heads;
+  const int hp = heads_per_workgroup(a.group);
+  const long blocks = (long)a.num_slots * (a.num_qo_heads / hp);
   if (blocks <= 0) return hipSuccess;
-  if (a.paged)
-    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
-  else
-    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(kWaves * 64), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(kWaves * 64);
+  if (a.paged) {
+    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<true, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<true, 1>), grid, block, 0, stream, a);
+  } else {
+    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<false, 4>), grid, block, 0, stream, a);
+    else hipLaunchKernelGGL((prefill_kernel<false, 1>), grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
-int prefill_rows_per_tile(int32_t window) {
+int prefill_rows_per_tile(int32_t window, int32_t group) {
   (void)window;
-  return kBM;
+  return kRowsPerWave * (kWaves / heads_per_workgroup(group));
 }
 
 }  // namespace sinkattn

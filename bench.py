@@ -371,8 +371,8 @@ def cpu_baseline(w, gpu_out):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the sharded layout is described "
-              "in DESIGN.md and not built", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); sharding the path over several "
+              "GPUs is not built", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():

@@ -1,0 +1,70 @@
+"""The entry points are documented as safe to capture in a HIP graph: they
+allocate nothing, never synchronise the host and keep no device state
+between calls.  Capture split decode + merge, prefill and a verify call
+into one graph, replay it several times with eager work in between, and
+check every replay against the eager results bit for bit."""
+
+import numpy as np
+import pytest
+
+from gqa_attention_sinks_amd import workloads as wl
+from tests._gpu import DeviceWorkload, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gqa_attention_sinks_amd as sa
+    sa.load_library()
+
+
+def test_graph_replay_matches_eager():
+    import torch
+    import gqa_attention_sinks_amd as sa
+    dec = DeviceWorkload(wl.paged_decode(batch=24, max_len=2000))
+    pre = DeviceWorkload(wl.make_contiguous("graph_prefill", [300, 129], [300, 64], 16, 2,
+                                            rng=np.random.default_rng(4)))
+    ver = DeviceWorkload(wl.verify_decode(batch=12, max_len=900))
+    dw, pw, vw = dec.w, pre.w, ver.w
+
+    outs = dict(dec=torch.empty_like(dec.q), pre=torch.empty_like(pre.q), ver=torch.empty_like(ver.q))
+    o_part = torch.empty((dw.batch, dw.num_qo_heads, 4, 64), dtype=torch.float32, device="cuda:0")
+    lse_part = torch.empty((dw.batch, dw.num_qo_heads, 4), dtype=torch.float32, device="cuda:0")
+    vo_part = torch.empty((int(vw.qo_indptr[-1]), vw.num_qo_heads, 3, 64), dtype=torch.float32, device="cuda:0")
+    vlse_part = torch.empty((int(vw.qo_indptr[-1]), vw.num_qo_heads, 3), dtype=torch.float32, device="cuda:0")
+
+    def work(stream=None):
+        sa.decode_paged(dec.q, dec.k, dec.v, dec.kv_indptr, dec.page_indices, dec.kv_len, dec.sinks, dw.scale,
+                        num_splits=4, out=outs["dec"], o_part=o_part, lse_part=lse_part, stream=stream)
+        sa.prefill(pre.q, pre.qo_indptr, pre.k, pre.v, pre.kv_indptr, pre.sinks, pw.scale, window=0,
+                   out=outs["pre"], stream=stream)
+        sa.decode_paged_multi(ver.q, ver.qo_indptr, ver.k, ver.v, ver.kv_indptr, ver.page_indices, ver.kv_len,
+                              ver.sinks, vw.scale, 8, num_splits=3, out=outs["ver"], o_part=vo_part,
+                              lse_part=vlse_part, stream=stream)
+
+    work()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        work(side)                        # warm the side stream once before capture
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            work(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for v in outs.values():           # eager work between replays
+            v.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in outs.items():
+            assert torch.equal(v, eager[k]), f"replay {rep}: {k} differs from the eager result"
+    say("graph replays match eager results")

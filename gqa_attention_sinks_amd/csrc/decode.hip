@@ -57,9 +57,10 @@ __device__ __forceinline__ int page_swizzle(int key, int chunk) {
 
 template <int NW, int NB>
 struct DecodeSmem {
-  // Several column blocks: Q operands staged once per workgroup (after the
-  // V staging area) and the waves merged one 16-column block at a time.
-  static constexpr bool kQInLds = NB >= 2;
+  // Q operands staged once per workgroup (after the V staging area), which
+  // frees registers for more waves; several column blocks are merged one
+  // 16-column block at a time.
+  static constexpr bool kQInLds = true;
   static constexpr int kStage = NW * kPageBytes;
   static constexpr int kQ = kQInLds ? NB * 2 * 64 * 16 : 0;
   static constexpr int kMerge = NW * 16 * (kQInLds ? 1 : NB) * (kHeadDim + 2) * 4;
@@ -136,7 +137,8 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
 // bit-packed custom mask per request (a draft tree) decides which keys each
 // row sees, instead of the causal rule.
 template <int NW, int PF, int NB, bool MULTI, bool MASK>
-__global__ __launch_bounds__(NW * 64) void decode_paged_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 7)))
+void decode_paged_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, NB>::kBytes];
 
   const int lane = threadIdx.x & 63;

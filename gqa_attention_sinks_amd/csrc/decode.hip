@@ -19,9 +19,11 @@
 //     O^T[64 dims x 16 heads] += V^T . P^T                 -> 4 x MFMA 16x16x16 fp16
 //       (P^T is the S^T accumulator converted in place to fp16; V is converted
 //        to fp16 and staged in LDS in its natural [key][dim] layout, then read
-//        back transposed with ds_read_b64_tr_b16).  The fp16 weights are taken
-//        relative to the running key maximum; the sink is folded in at the end,
-//        which gives exactly the state of the sink-seeded recurrence.
+//        back transposed with ds_read_b64_tr_b16).  The Q^T operands are staged
+//        in LDS once per workgroup.  The fp16 weights are taken relative to the
+//        running key maximum (one row) or to a reference that moves only when
+//        a weight would overflow (several rows); the sink is folded in at the
+//        end, which gives exactly the state of the sink-seeded recurrence.
 //   Each chunk's result is normalised by its own denominator and written as an
 //   fp32 partial with its natural-log LSE, or, unsplit, as the bf16 output.
 //   Several query rows per request (a speculative verify step, "Accelerating
@@ -55,15 +57,14 @@ __device__ __forceinline__ int page_swizzle(int key, int chunk) {
   return key * 128 + ((chunk ^ (key & 7)) << 4);
 }
 
+// LDS of a workgroup: per-wave V staging pages, then the Q^T operands
+// (staged once, read every page: registers go to more waves); after the page
+// loop the same bytes hold the cross-wave merge of one 16-column block.
 template <int NW, int NB>
 struct DecodeSmem {
-  // Q operands staged once per workgroup (after the V staging area), which
-  // frees registers for more waves; several column blocks are merged one
-  // 16-column block at a time.
-  static constexpr bool kQInLds = true;
   static constexpr int kStage = NW * kPageBytes;
-  static constexpr int kQ = kQInLds ? NB * 2 * 64 * 16 : 0;
-  static constexpr int kMerge = NW * 16 * (kQInLds ? 1 : NB) * (kHeadDim + 2) * 4;
+  static constexpr int kQ = NB * 2 * 64 * 16;
+  static constexpr int kMerge = NW * 16 * (kHeadDim + 2) * 4;
   static constexpr int kBytes = kStage + kQ > kMerge ? kStage + kQ : kMerge;
 };
 
@@ -137,7 +138,7 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
 // bit-packed custom mask per request (a draft tree) decides which keys each
 // row sees, instead of the causal rule.
 template <int NW, int PF, int NB, bool MULTI, bool MASK>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MULTI ? 1 : 7)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MULTI || PF > 1 ? 1 : 7)))
 void decode_paged_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, NB>::kBytes];
 
@@ -190,14 +191,9 @@ void decode_paged_kernel(DecodeArgs a) {
   const int full_hi = min(t_hi - 1, n_k - n_q);
 
   // This lane's columns: Q^T operands of the score MFMA (column = (row, head),
-  // k = dims 16*grp + 8*ks + e) and, with several rows, each column's own
-  // visible key range [c_lo, c_pos].
-  // With several column blocks the operands live in LDS (loaded once by
-  // wave 0, read per page), which keeps the register count at three waves
-  // per SIMD; one block stays in registers.
-  constexpr bool kQLds = DecodeSmem<NW, NB>::kQInLds;
-  constexpr int QR = kQLds ? 1 : NB;
-  bf16x8 q0[QR], q1[QR];
+  // k = dims 16*grp + 8*ks + e), loaded once by wave 0 into LDS and read from
+  // there every page, and, with several rows, each column's own visible key
+  // range [c_lo, c_pos].
   int c_lo[NB], c_pos[NB];
   int c_bit[NB];   // MASK: bit offset of the column's mask row in the request's mask (-1: no row)
   u32x4* const q_lds = reinterpret_cast<u32x4*>(smem + DecodeSmem<NW, NB>::kStage);   // [NB][2][64 lanes]
@@ -206,29 +202,23 @@ void decode_paged_kernel(DecodeArgs a) {
     const int j = 16 * nb + col;
     const int t = j / G;
     const int head = g * G + (j - t * G);
-    if (!kQLds || wave == 0) {
-      bf16x8 x0 = {}, x1 = {};
+    if (wave == 0) {
+      u32x4 x0 = {}, x1 = {};
       if (t < n_q) {
         const uint16_t* qp = a.q + ((size_t)(qrow + t) * a.num_qo_heads + head) * kHeadDim + 16 * grp;
-        x0 = __builtin_bit_cast(bf16x8, ldg16(qp));
-        x1 = __builtin_bit_cast(bf16x8, ldg16(qp + 8));
+        x0 = ldg16(qp);
+        x1 = ldg16(qp + 8);
       }
-      if (kQLds) {
-        q_lds[(nb * 2) * 64 + lane] = __builtin_bit_cast(u32x4, x0);
-        q_lds[(nb * 2 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, x1);
-      } else {
-        q0[nb < QR ? nb : 0] = x0;
-        q1[nb < QR ? nb : 0] = x1;
-      }
+      q_lds[(nb * 2) * 64 + lane] = x0;
+      q_lds[(nb * 2 + 1) * 64 + lane] = x1;
     }
     c_pos[nb] = n_k - n_q + t;
     c_lo[nb] = a.window > 0 ? c_pos[nb] - a.window + 1 : 0;
     c_bit[nb] = t < n_q ? t * n_k : -1;
   }
-  if (kQLds) __syncthreads();
+  __syncthreads();
   auto qop = [&](int nb, int half) -> bf16x8 {
-    if (kQLds) return __builtin_bit_cast(bf16x8, q_lds[(nb * 2 + half) * 64 + lane]);
-    return half ? q1[nb < QR ? nb : 0] : q0[nb < QR ? nb : 0];
+    return __builtin_bit_cast(bf16x8, q_lds[(nb * 2 + half) * 64 + lane]);
   };
   // the request's mask: row t, key j is bit t * n_k + j (little-endian bytes)
   const uint8_t* mbytes = MASK ? a.custom_mask + a.mask_indptr[b] : nullptr;
@@ -434,8 +424,8 @@ void decode_paged_kernel(DecodeArgs a) {
     dsum[nb] += shfl_xor_f32(dsum[nb], 32);
   }
 
-  // merge the waves through LDS, kMB column blocks at a time
-  constexpr int kMB = kQLds ? 1 : NB;
+  // merge the waves through LDS, one 16-column block at a time
+  constexpr int kMB = 1;
   constexpr int kCols = 16 * kMB;
   float* sm_m = reinterpret_cast<float*>(smem);
   float* sm_d = sm_m + NW * kCols;

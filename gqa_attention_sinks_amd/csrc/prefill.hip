@@ -11,7 +11,8 @@
 //   query heads that share a KV head when the GQA group splits into fours
 //   (every wave then needs exactly the workgroup's key tiles), else 256
 //   consecutive rows of one head.  Two workgroups per CU, so each SIMD runs
-//   two waves whose matrix and vector phases overlap.  Consecutive workgroup
+//   two waves (one of each); inside a wave the matrix steps are interleaved
+//   with the vector work of the other half tile.  Consecutive workgroup
 //   ids walk the KV heads first, so with 8 KV heads and 8 XCDs each XCD's L2
 //   serves one KV head.  Tiles of a request are issued longest first (causal
 //   work grows with the row index).

@@ -40,8 +40,9 @@ struct MergeArgs {
   int32_t rows, num_heads, num_splits;
 };
 
-// Causal / sliding-window prefill, one query head and a tile of query rows
-// per workgroup.
+// Causal / sliding-window prefill: a workgroup takes one tile of query rows
+// of one query head, or of four heads of one group when the group size is a
+// multiple of four.
 struct PrefillArgs {
   const uint16_t* q;          // [total_q, Hq, 64]
   const int32_t* qo_indptr;   // [B+1]

@@ -239,6 +239,35 @@ def time_verify(w, args, torch, dev):
     return dict(step_ms=wall * 1e3, decode_ms=e0.elapsed_time(e1) / args.steps, splits=s)
 
 
+def per_call_ms(call, args, torch):
+    """Time per call of a short kernel.  ``ms``: ``args.steps`` calls captured
+    in one HIP graph and replayed, so the host's launch rate does not enter
+    (these kernels run for a few microseconds, about what a launch from Python
+    costs); ``ms_eager``: the same calls issued one by one from Python."""
+    for _ in range(args.warmup):
+        call()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = e0.elapsed_time(e1) / args.steps
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(args.steps):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / args.steps, ms_eager
+
+
 def time_append(args, torch, dev):
     """Paged KV append with rotary embedding of queries and keys
     (sinkattn_append_paged_kv_rope): 16 prefill chunks of 512 tokens on
@@ -264,19 +293,9 @@ def time_append(args, torch, dev):
     table = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to(dev)
     q_out = torch.empty_like(q)
     args_ = (k, v, i32(append_indptr), kp, vp, i32(page_indptr), i32(page_indices), i32(kv_len), table)
-    for _ in range(args.warmup):
-        sa.append_paged_kv_rope(*args_, q=q, q_out=q_out)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        sa.append_paged_kv_rope(*args_, q=q, q_out=q_out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_eager = per_call_ms(lambda: sa.append_paged_kv_rope(*args_, q=q, q_out=q_out), args, torch)
     nbytes = t * (2 * hq * 128 + 4 * hkv * 128 + 256) + 4 * (len(page_indices) + 3 * 17)
-    return dict(tokens=t, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
+    return dict(tokens=t, ms=ms, ms_eager=ms_eager, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
 
 
 def time_moe(args, torch, dev):
@@ -289,19 +308,10 @@ def time_moe(args, torch, dev):
     logits = logits.view(torch.bfloat16)
     idx = torch.empty((t, k), dtype=torch.int32, device=dev)
     w = torch.empty((t, k), dtype=torch.bfloat16, device=dev)
-    for _ in range(args.warmup):
-        sa.moe_topk_softmax(logits, k, idx, w)
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        sa.moe_topk_softmax(logits, k, idx, w)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms, ms_eager = per_call_ms(lambda: sa.moe_topk_softmax(logits, k, idx, w), args, torch)
     nbytes = t * (e * 2 + k * 6)
-    return dict(tokens=t, experts=e, top_k=k, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
+    return dict(tokens=t, experts=e, top_k=k, ms=ms, ms_eager=ms_eager, bytes=nbytes,
+                GBs=nbytes / (ms * 1e-3) / 1e9)
 
 
 def time_prefill(w, steps, warmup, torch, dev, window=0):

@@ -9,10 +9,13 @@
 //
 // Eight lanes per token (eight tokens per wave).  Each logit becomes a
 // 32-bit key: the bf16 bits mapped to an unsigned order (larger logit, larger
-// key) in the high half and the complemented expert index in the low half, so
-// one unsigned comparison orders by logit and, among equal logits, puts the
-// lower index first.  Each lane keeps the top KP keys of its own experts in a
-// descending register list (an insertion per key); three exchange levels
+// key; -0 and +0 the same) in the high half and the complemented expert index
+// in the low half, so one unsigned comparison orders by logit and, among equal
+// logits, puts the lower index first.  Each lane keeps the top KP keys of its
+// own experts in a descending register list; inserting a key costs one
+// three-input median per list entry (entry i becomes the median of the old
+// entries i - 1 and i and the key), and the map needs no compare-and-select,
+// so the loop is plain integer arithmetic.  Three exchange levels
 // (lanes 1, 2, 4 apart) merge the eight lists: the elementwise max of a list
 // and its partner's reversed list holds the top KP of both, and a bitonic
 // network sorts it.  Every lane then holds the token's top KP; lane s < K
@@ -30,18 +33,34 @@ __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
   return (uint32_t)__builtin_amdgcn_ds_bpermute(src << 2, (int)v);
 }
 
-__device__ __forceinline__ uint32_t order_key(uint16_t bits, int expert) {
-  if (bits == 0x8000u) bits = 0;   // -0 equals +0: the same key, so the index decides
-  // sign-magnitude -> unsigned order: negatives reversed below positives
-  const uint32_t ord = (bits & 0x8000u) ? (uint32_t)(~bits & 0xffffu) : (uint32_t)(bits | 0x8000u);
-  return (ord << 16) | (uint32_t)(0xffff - expert);
+// Order key of a logit whose bf16 bits sit in the high half of x (low half
+// zero), with idx = 0xffff - expert added in the low half.  A non-negative
+// value v maps to v + 2^31, a negative one to -v (two's complement, below
+// 2^31), so the map is monotone and -0 lands on +0's key.
+__device__ __forceinline__ uint32_t order_key(uint32_t x, uint32_t idx) {
+  const uint32_t s = (uint32_t)((int32_t)x >> 31);   // all ones for a negative value
+  return (((x ^ s) - s) ^ (~s & 0x80000000u)) + idx;
+}
+
+// The same map on both bf16 halves of w at once (16-bit lanes): the high
+// halves of the two keys, in the low and high half of the result.
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 order_hi_pair(uint32_t w) {
+  const u16x2 b = __builtin_bit_cast(u16x2, w);
+  const u16x2 s = __builtin_bit_cast(u16x2, __builtin_bit_cast(s16x2, b) >> (short)15);
+  return ((b ^ s) - s) ^ (~s & (unsigned short)0x8000);
 }
 
 // the logit of a key (inverse of the order map), as fp32
 __device__ __forceinline__ float key_logit(uint32_t key) {
-  const uint32_t ord = key >> 16;
-  const uint32_t bits = (ord & 0x8000u) ? (ord ^ 0x8000u) : (~ord & 0xffffu);
-  return __builtin_bit_cast(float, bits << 16);
+  const uint32_t hi = key & 0xffff0000u;
+  const uint32_t bits = (hi & 0x80000000u) ? (hi ^ 0x80000000u) : (0u - hi);
+  return __builtin_bit_cast(float, bits);
+}
+
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
 }
 
 template <int KP>
@@ -69,13 +88,10 @@ __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
   uint32_t top[KP];                                          // descending; 0 is below every key
 #pragma unroll
   for (int i = 0; i < KP; ++i) top[i] = 0u;
-  auto insert = [&](uint32_t key) {
+  auto insert = [&](uint32_t key) {                          // top KP of the list and the key
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {                           // larger keys move up
-      const uint32_t hi = max(top[i], key);
-      key = min(top[i], key);
-      top[i] = hi;
-    }
+    for (int i = KP - 1; i >= 1; --i) top[i] = umed3(top[i - 1], top[i], key);
+    top[0] = max(top[0], key);
   };
   if (live) {
     const uint16_t* row = a.logits + t * a.num_experts;
@@ -91,12 +107,14 @@ __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
         if (c >= nch) break;
 #pragma unroll
         for (int w = 0; w < 4; ++w) {
-          insert(order_key((uint16_t)(ch[c][w] & 0xffffu), e0 + 8 * c + 2 * w));
-          insert(order_key((uint16_t)(ch[c][w] >> 16), e0 + 8 * c + 2 * w + 1));
+          const uint32_t idx = 0xffffu - (uint32_t)(e0 + 8 * c + 2 * w);
+          const uint32_t k2 = __builtin_bit_cast(uint32_t, order_hi_pair(ch[c][w]));
+          insert((k2 << 16) | idx);
+          insert((k2 & 0xffff0000u) | (idx - 1));
         }
       }
     } else {
-      for (int e = e0; e < e1; ++e) insert(order_key(row[e], e));
+      for (int e = e0; e < e1; ++e) insert(order_key((uint32_t)row[e] << 16, 0xffffu - (uint32_t)e));
     }
   }
   // merge the eight lists of the token's lanes (every lane takes part: the

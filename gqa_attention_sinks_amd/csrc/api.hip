@@ -273,8 +273,10 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
                                               int32_t total_new, int32_t num_qo_heads,
                                               int32_t num_kv_heads, int32_t head_dim,
                                               void* stream) {
-  REQUIRE(k_new != nullptr && v_new != nullptr && append_indptr != nullptr && cos_sin != nullptr,
-          SINKATTN_ERR_INVALID_ARG, "k_new, v_new, append_indptr and cos_sin are required");
+  // with no new token nothing is read or written, so the token buffers may be NULL
+  REQUIRE((total_new == 0 || (k_new != nullptr && v_new != nullptr)) && append_indptr != nullptr &&
+              cos_sin != nullptr,
+          SINKATTN_ERR_INVALID_ARG, "k_new, v_new (unless total_new == 0), append_indptr and cos_sin are required");
   REQUIRE((q == nullptr) == (q_out == nullptr), SINKATTN_ERR_INVALID_ARG,
           "q and q_out must be given together (or both NULL)");
   sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, 1.0f, 0);
@@ -307,8 +309,9 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
 
 sinkattn_status sinkattn_moe_topk_softmax(const void* logits, int32_t num_tokens, int32_t num_experts,
                                           int32_t top_k, int32_t* topk_idx, void* topk_w, void* stream) {
-  REQUIRE(logits != nullptr && topk_idx != nullptr && topk_w != nullptr, SINKATTN_ERR_INVALID_ARG,
-          "logits, topk_idx and topk_w are required");
+  // with no token nothing is read or written, so the buffers may be NULL
+  REQUIRE(num_tokens == 0 || (logits != nullptr && topk_idx != nullptr && topk_w != nullptr),
+          SINKATTN_ERR_INVALID_ARG, "logits, topk_idx and topk_w are required");
   REQUIRE(num_tokens >= 0, SINKATTN_ERR_INVALID_ARG, "num_tokens must be >= 0 (got %d)", num_tokens);
   REQUIRE(num_experts >= 1 && num_experts <= SINKATTN_MAX_EXPERTS, SINKATTN_ERR_UNSUPPORTED,
           "num_experts must be in [1, %d] (got %d)", SINKATTN_MAX_EXPERTS, num_experts);

@@ -219,10 +219,12 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
  *   kv       paged descriptor (kv->paged must be 1); its pools are written at
  *            the new tokens' slots only
  *   cos_sin  [max_pos, 64] fp32 (device, 16-byte aligned)
- *   q_out    [total_q, Hq, 64] bf16, written (may equal q); NULL when q is NULL
+ *   q_out    [total_new, Hq, 64] bf16, written (may equal q); NULL when q is NULL
  * Results are rounded to bf16 from fp32 arithmetic; values are copied
  * exactly.  A token whose position falls outside [0, max_pos) is not written
- * (its query row either).  Two appends that hit the same slot race. */
+ * (its query row either).  Two appends that hit the same slot race.  With
+ * total_new == 0 nothing is read or written and k_new, v_new, q and q_out may
+ * be NULL. */
 sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, const void* v_new,
                                               const int32_t* append_indptr, const sinkattn_kv* kv,
                                               const float* cos_sin, int32_t max_pos,
@@ -244,7 +246,8 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
  *             first
  *   topk_w    [num_tokens, top_k] bf16, written: the weights, same order
  *   1 <= num_experts <= SINKATTN_MAX_EXPERTS, 1 <= top_k <=
- *   min(SINKATTN_MAX_TOP_K, num_experts). */
+ *   min(SINKATTN_MAX_TOP_K, num_experts).  With num_tokens == 0 nothing is
+ *   read or written and the three buffers may be NULL. */
 sinkattn_status sinkattn_moe_topk_softmax(const void* logits, int32_t num_tokens, int32_t num_experts,
                                           int32_t top_k, int32_t* topk_idx, void* topk_w, void* stream);
 

@@ -208,6 +208,15 @@ def test_append_needs_paged(lib):
     assert _append(lib, _kv(paged=0)) == INVALID
 
 
+def test_zero_sized_calls_accept_null_buffers(lib):
+    # nothing to read or write: the token buffers may be NULL and nothing is launched
+    assert _append(lib, _kv(), k=None, v=None, total=0) == 0
+    assert _append(lib, _kv(), k=None, v=FAKE, total=1) == INVALID
+    assert lib.sinkattn_moe_topk_softmax(None, 0, 32, 4, None, None, None) == 0
+    assert lib.sinkattn_moe_topk_softmax(None, 1, 32, 4, FAKE, FAKE, None) == INVALID
+    assert lib.sinkattn_moe_topk_softmax(None, 0, 32, 33, None, None, None) == INVALID
+
+
 @pytest.mark.parametrize("args,code", [
     ((None, 4, 32, 4, FAKE, FAKE), INVALID),
     ((FAKE, 4, 32, 4, None, FAKE), INVALID),

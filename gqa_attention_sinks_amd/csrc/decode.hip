@@ -45,6 +45,9 @@ constexpr int kPageBytes = kPageSize * kHeadDim * 2;  // one (page, KV head) blo
 // would exceed this (fp16 keeps them finite, the rescale stays rare)
 constexpr float kWeightLimit = 16384.f;
 constexpr float kFloatMax = 3.402823466e38f;
+// s_waitcnt operand: vector memory count 0, the other counters unconstrained
+// (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = 0x0F70;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -247,24 +250,45 @@ void decode_paged_kernel(DecodeArgs a) {
   uint8_t* stage = smem + wave * kPageBytes;
 
   // Ring of PF pages in flight: slot u holds page lp + u of the current
-  // round.  The wave's page ids arrive as one vector load (lane i holds the
-  // id of page wp0 + 64*k + i, reloaded every 64 pages), issued together
-  // with Q, and each step reads its id with readlane: no per-page scalar load
-  // and only one id latency in front of the first page.
+  // round.  The wave's page ids arrive as vector loads, one lane per page, and
+  // each step reads its id with readlane: no per-page scalar load and only one
+  // id latency in front of the first page.  The wave's pages form groups of
+  // 64; the ids of even groups live in ids0, of odd groups in ids1.  When
+  // processing enters group g, the register of group g - 1 is reloaded with
+  // group g + 1, 64 pages before its first use, so no id read on the common
+  // path depends on a load of the same round.
+  //
+  // With several pages in flight every path through the page loop must issue
+  // the same loads in the same order, or the compiler's count of loads in
+  // flight turns conservative and waits for all of them before each page:
+  // past the end of the wave's run a slot is refilled with the run's last
+  // page again (a cache hit) rather than skipped.
   u32x4 kc[PF][2], vc[PF][2];
   uint32_t mk[PF][NB];   // MASK: this lane's four mask bits per column block
-  int id_vec = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
-  int id_base = wp0;                      // page index of id_vec's lane 0
-  auto page_id = [&](int p) -> int {      // p uniform, wp0 <= p < id_base + 64
-    return __builtin_amdgcn_readlane(id_vec, p - id_base);
+  int ids0 = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
+  int ids1 = 64 + lane < wp1 - wp0 ? pages[wp0 + 64 + lane] : 0;
+  // The id loads complete here and in each (rare) reload below, so that no
+  // id register is ever seen as pending inside the page loop.
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  int next_group = 1;                     // the group whose entry triggers the next reload
+  auto page_id = [&](int p) -> int {      // p uniform, in group next_group or the one before
+    const int r = p - wp0;
+    return ((r >> 6) & 1) ? __builtin_amdgcn_readlane(ids1, r & 63) : __builtin_amdgcn_readlane(ids0, r & 63);
   };
-  auto load_page = [&](int u, int p) {
-    if (p < wp1) {
-      if (p - id_base >= 64) {            // uniform: next 64 ids
-        id_base += 64;
-        id_vec = id_base + lane < wp1 ? pages[id_base + lane] : 0;
-      }
-      const size_t off = (size_t)page_id(p) * page_stride;
+  auto advance_ids = [&](int p) {         // p: the page being processed (uniform)
+    const int g = (p - wp0) >> 6;
+    if (g == next_group) {
+      ++next_group;
+      const int base = wp0 + 64 * (g + 1);
+      if (g & 1) ids0 = base + lane < wp1 ? pages[base + lane] : 0;
+      else ids1 = base + lane < wp1 ? pages[base + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+  };
+  auto load_page = [&](int u, int p) {   // several in flight: only while the run has pages
+    if (PF > 1 || p < wp1) {
+      const int pc = PF > 1 ? min(p, wp1 - 1) : p;
+      const size_t off = (size_t)page_id(pc) * page_stride;
       const uint16_t* kp = kpool + off + lane_off;
       const uint16_t* vp = vpool + off + lane_off;
       kc[u][0] = ldg16(kp);
@@ -274,7 +298,7 @@ void decode_paged_kernel(DecodeArgs a) {
       if (MASK) {
         // keys key0 .. key0 + 3 of this lane; the bytes read stop at the
         // request's last key, so they stay inside its mask
-        const int key0 = p * kPageSize + 4 * grp;
+        const int key0 = pc * kPageSize + 4 * grp;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
           mk[u][nb] = 0;
@@ -289,14 +313,16 @@ void decode_paged_kernel(DecodeArgs a) {
       }
     }
   };
+  if (PF == 1 || wp0 < wp1) {
 #pragma unroll
-  for (int u = 0; u < PF; ++u) load_page(u, wp0 + u);
+    for (int u = 0; u < PF; ++u) load_page(u, wp0 + u);
+  }
 
-  for (int lp = wp0; lp < wp1; lp += PF) {
-#pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int p = lp + u;
-      if (p >= wp1) break;
+  // One page: ring slot u holds page p.  With several pages in flight, full
+  // rounds of PF pages run in the main loop and the last, partial round after
+  // it, so that every path through the loop body leaves the slots' loads in
+  // flight in the same order.
+  auto page_step = [&](const int u, const int p) __attribute__((always_inline)) {
       // scores of page p (ring slot u), every column block
       f32x4 sc[NB];
 #pragma unroll
@@ -306,12 +332,19 @@ void decode_paged_kernel(DecodeArgs a) {
         sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][0]), qop(nb, 0), sc[nb], 0, 0, 0);
         sc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kc[u][1]), qop(nb, 1), sc[nb], 0, 0, 0);
       }
-      const u32x4 v0r = vc[u][0], v1r = vc[u][1];
       uint32_t mcur[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) mcur[nb] = MASK ? mk[u][nb] : 0u;
-      // the slot is free once its registers are consumed: refill it
-      load_page(u, p + PF);
+      // One page in flight: the slot is free once its registers are copied,
+      // so refill it now.  Several: refill after V is staged (no copy, and no
+      // wait on the other slots' loads).
+      u32x4 v0r, v1r;
+      if constexpr (PF == 1) {
+        v0r = vc[u][0];
+        v1r = vc[u][1];
+        advance_ids(p);
+        load_page(u, p + PF);
+      }
 
       const int key0 = p * kPageSize + 4 * grp;
       // uniform: every key of the page visible to every column (no per-key test)
@@ -393,12 +426,16 @@ void decode_paged_kernel(DecodeArgs a) {
       u32x4 v0, v1;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        v0[e] = bf16x2_to_f16x2(v0r[e]);
-        v1[e] = bf16x2_to_f16x2(v1r[e]);
+        v0[e] = bf16x2_to_f16x2(PF == 1 ? v0r[e] : vc[u][0][e]);
+        v1[e] = bf16x2_to_f16x2(PF == 1 ? v1r[e] : vc[u][1][e]);
       }
       if (p * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
       *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp)) = v0;
       *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp + 1)) = v1;
+      if constexpr (PF > 1) {
+        advance_ids(p);
+        load_page(u, p + PF);
+      }
       __asm__ volatile("" ::: "memory");
       // transposed read: lane (grp, j) addresses key 4*grp + j/4, dims 16*db + 4*(j%4)
       const int rkey = 4 * grp + (col >> 2);
@@ -414,7 +451,18 @@ void decode_paged_kernel(DecodeArgs a) {
             acc[nb][db] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vt), pb[nb], acc[nb][db], 0, 0, 0);
       }
       __asm__ volatile("" ::: "memory");
+  };
+  if constexpr (PF == 1) {
+    for (int p = wp0; p < wp1; ++p) page_step(0, p);
+  } else {
+    int lp = wp0;
+    for (; lp + PF <= wp1; lp += PF) {
+#pragma unroll
+      for (int u = 0; u < PF; ++u) page_step(u, lp + u);
     }
+#pragma unroll
+    for (int u = 0; u + 1 < PF; ++u)
+      if (lp + u < wp1) page_step(u, lp + u);
   }
 
   // the four lanes of a column hold partial denominators

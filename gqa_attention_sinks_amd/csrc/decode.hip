@@ -131,6 +131,15 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
   return u;
 }
 
+// Waves per SIMD each variant is held to (so that a register-count change
+// cannot silently lower occupancy; a variant that no longer fits spills, and
+// the no-spill check of the build's tests fails): one page in flight with one
+// row fits seven; the multi-row variants hold about 80, 110 and 160 VGPRs for
+// one, two and four column blocks.
+constexpr int decode_waves_per_simd(int PF, int NB, bool MULTI) {
+  return PF > 1 ? 1 : !MULTI ? 7 : NB == 1 ? 6 : NB == 2 ? 4 : 3;
+}
+
 // PF: pages in flight per wave (a ring of register buffers; the loop is
 // unrolled by PF so the ring slots are static).  NB: 16-column blocks of the
 // MFMAs.  Column j of the blocks is (query row j / G, query head j % G) of
@@ -141,7 +150,7 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
 // bit-packed custom mask per request (a draft tree) decides which keys each
 // row sees, instead of the causal rule.
 template <int NW, int PF, int NB, bool MULTI, bool MASK>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(MULTI || PF > 1 ? 1 : 7)))
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(decode_waves_per_simd(PF, NB, MULTI))))
 void decode_paged_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[DecodeSmem<NW, NB>::kBytes];
 
@@ -195,9 +204,10 @@ void decode_paged_kernel(DecodeArgs a) {
 
   // This lane's columns: Q^T operands of the score MFMA (column = (row, head),
   // k = dims 16*grp + 8*ks + e), loaded once by wave 0 into LDS and read from
-  // there every page, and, with several rows, each column's own visible key
-  // range [c_lo, c_pos].
-  int c_lo[NB], c_pos[NB];
+  // there every page, and the keys of the chunk each column may see,
+  // [v_lo, v_hi] (with several rows: its own causal / window range; a mask,
+  // where given, decides inside it).
+  int v_lo[NB], v_hi[NB];
   int c_bit[NB];   // MASK: bit offset of the column's mask row in the request's mask (-1: no row)
   u32x4* const q_lds = reinterpret_cast<u32x4*>(smem + DecodeSmem<NW, NB>::kStage);   // [NB][2][64 lanes]
 #pragma unroll
@@ -215,8 +225,10 @@ void decode_paged_kernel(DecodeArgs a) {
       q_lds[(nb * 2) * 64 + lane] = x0;
       q_lds[(nb * 2 + 1) * 64 + lane] = x1;
     }
-    c_pos[nb] = n_k - n_q + t;
-    c_lo[nb] = a.window > 0 ? c_pos[nb] - a.window + 1 : 0;
+    const int c_pos = n_k - n_q + t;
+    const int c_lo = a.window > 0 ? c_pos - a.window + 1 : 0;
+    v_lo[nb] = MULTI && !MASK ? max(t_lo, c_lo) : t_lo;
+    v_hi[nb] = MULTI && !MASK ? min(t_hi - 1, c_pos) : t_hi - 1;
     c_bit[nb] = t < n_q ? t * n_k : -1;
   }
   __syncthreads();
@@ -356,9 +368,8 @@ void decode_paged_kernel(DecodeArgs a) {
         if (nb >= nb_used) continue;
         auto visible = [&](int i) -> bool {
           const int j = key0 + i;
-          bool vis = j >= t_lo && j < t_hi;
+          bool vis = j >= v_lo[nb] && j <= v_hi[nb];
           if (MASK) vis = vis && ((mcur[nb] >> i) & 1u);
-          else if (MULTI) vis = vis && j >= c_lo[nb] && j <= c_pos[nb];
           return vis;
         };
         // scaled scores (base 2) of the lane's four keys, -inf where not visible
@@ -374,14 +385,19 @@ void decode_paged_kernel(DecodeArgs a) {
           // visible page, m starting at -FLT_MAX): move the reference to the
           // column maxima, rescale, and redo the weights.
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            pw[i] = exp2_hw(__builtin_fmaf(sc[nb][i], a.scale_log2, -m[nb]));
-            if (!page_full && !visible(i)) pw[i] = 0.f;
+          for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(__builtin_fmaf(sc[nb][i], a.scale_log2, -m[nb]));
+          if (!page_full) {   // uniform: one branch per block, selects inside
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pw[i] = visible(i) ? pw[i] : 0.f;
           }
           const float pmax = fmaxf(fmaxf(pw[0], pw[1]), fmaxf(pw[2], pw[3]));
           if (__builtin_amdgcn_ballot_w64(pmax > kWeightLimit) != 0) {
+            // the keys that can move the reference are those with a nonzero
+            // weight: a hidden key's weight is 0, and one that underflowed
+            // lies far below the reference
             float s4[4];
-            masked_scores(s4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s4[i] = pw[i] > 0.f ? sc[nb][i] * a.scale_log2 : kNegInf;
             float tile_max = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
             tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 16));
             tile_max = fmaxf(tile_max, shfl_xor_f32(tile_max, 32));

@@ -132,12 +132,17 @@ __device__ __forceinline__ int tile_work(int n_q, int n_k, int t, int window) {
   return (shift + t_last + 1 - k_first + kBN - 1) / kBN;
 }
 
+// Under a window up to this long every query tile carries about the same
+// work (at most a few key tiles), and ranking would only cost time.
+constexpr int kRankMinWindow = 2048;
+
 // Find the (request, tile) handled by tile slot `slot`.  Tiles are numbered
 // request by request (every thread sums a run of requests, then a block
-// scan).  When the requests differ in shape and the batch has at most 256
-// query tiles, the slots take the tiles in order of decreasing work (ties by
-// number), so the longest tiles of every request start first and the short
-// ones fill the tail.  Otherwise they take them request by request, longest
+// scan).  When the requests differ in shape, the batch has at most 256
+// query tiles and the window is unbounded or longer than kRankMinWindow, the
+// slots take the tiles in order of decreasing work (ties by number), so the
+// longest tiles of every request start first and the short ones fill the
+// tail.  Otherwise they take them request by request, longest
 // tile first: with equal requests that order is as balanced, and tiles of
 // one request that run together share its keys in L2.
 template <int RT>
@@ -178,7 +183,7 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   const int total = s_scan[kThreads - 1];
   __shared__ int s_found[2];
   if (tid == 0) s_found[0] = -1;
-  if (total <= kThreads && !uniform) {
+  if (total <= kThreads && !uniform && (a.window == 0 || a.window > kRankMinWindow)) {
     // list every (request, tile) with its work, then rank
     __shared__ int s_work[kThreads];
     __shared__ int s_req[kThreads];

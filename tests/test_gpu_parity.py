@@ -246,15 +246,16 @@ def test_prefill_many_tiles_request_major(uniform):
 
 
 def test_prefill_uneven_ranked_order_windowed():
-    """Uneven requests with at most 256 tiles take the ranked order; also
-    with a window."""
+    """Uneven requests with at most 256 tiles take the ranked order without a
+    window and under a window longer than 2048 keys; under a short window
+    (200) they take request order."""
     rng = np.random.default_rng(33)
     qo_len = np.array([600, 20, 513, 256, 1000, 3])
     kv_len = qo_len + np.array([0, 700, 5, 300, 0, 2000])
     w = wl.make_paged("ranked", kv_len, qo_len, 8, 2, rng=rng)
-    say("prefill uneven requests, ranked order, windows 0 and 200")
+    say("prefill uneven requests, windows 0, 200 and 3000")
     d = DeviceWorkload(w)
-    for window in [0, 200]:
+    for window in [0, 200, 3000]:
         out, lse = d.prefill(window=window)
         ro, rl = oracle_full(w, window)
         assert_parity(to_host(out), ro, f"prefill ranked W={window}", to_host(lse), rl)

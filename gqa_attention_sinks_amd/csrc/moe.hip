@@ -76,13 +76,13 @@ __device__ __forceinline__ void sort_bitonic_desc(uint32_t (&m)[KP]) {
       }
 }
 
-template <int KP>
+template <int KP, int L>
 __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
   const int lane = threadIdx.x & 63;
-  const int s = lane & 7;                                    // this lane's share of the experts
-  const long t = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 8 + (lane >> 3);
+  const int s = lane % L;                                    // this lane's share of the experts
+  const long t = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 / L) + lane / L;
   const bool live = t < a.num_tokens;
-  const int per = (a.num_experts + 7) / 8;
+  const int per = (a.num_experts + L - 1) / L;
   const int e0 = s * per, e1 = min(e0 + per, a.num_experts);
 
   uint32_t top[KP];                                          // descending; 0 is below every key
@@ -95,9 +95,9 @@ __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
   };
   if (live) {
     const uint16_t* row = a.logits + t * a.num_experts;
-    if (a.num_experts % 64 == 0) {
+    if (a.num_experts % (8 * L) == 0) {
       // whole 16-byte chunks (8 logits) per lane, all loads issued first
-      const int nch = per / 8;                               // 1 .. 8
+      const int nch = per / 8;                               // 1 .. 8 (the launch keeps E <= 64 L)
       u32x4 ch[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -117,10 +117,10 @@ __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
       for (int e = e0; e < e1; ++e) insert(order_key((uint32_t)row[e] << 16, 0xffffu - (uint32_t)e));
     }
   }
-  // merge the eight lists of the token's lanes (every lane takes part: the
-  // exchanges stay inside each 8-lane group)
+  // merge the L lists of the token's lanes (every lane takes part: the
+  // exchanges stay inside each L-lane group)
 #pragma unroll
-  for (int m = 1; m < 8; m <<= 1) {
+  for (int m = 1; m < L; m <<= 1) {
     uint32_t other[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) other[i] = shfl_xor_u32(top[i], m);
@@ -129,34 +129,43 @@ __global__ __launch_bounds__(256) void moe_topk_softmax_kernel(MoeArgs a) {
     sort_bitonic_desc<KP>(top);
   }
   if (!live || s >= a.top_k) return;
-  // softmax over the K selected logits (each lane sums them itself)
+  // softmax over the K selected logits (each lane sums them itself); lane s
+  // writes entries s, s + L, ...
   const float l0 = key_logit(top[0]);
-  float sum = 0.f, mine = 0.f;
-  uint32_t my_key = top[0];
+  float ex[KP];
+  float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < KP; ++i) {
-    if (i >= a.top_k) break;
-    const float ex = exp2_hw((key_logit(top[i]) - l0) * kLog2e);
-    sum += ex;
-    if (i == s) {
-      mine = ex;
-      my_key = top[i];
-    }
+    ex[i] = i < a.top_k ? exp2_hw((key_logit(top[i]) - l0) * kLog2e) : 0.f;
+    sum += ex[i];
   }
-  a.topk_idx[t * a.top_k + s] = 0xffff - (int)(my_key & 0xffffu);
-  a.topk_w[t * a.top_k + s] = to_bf16_bits(mine / sum);
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    if (i % L != s || i >= a.top_k) continue;
+    a.topk_idx[t * a.top_k + i] = 0xffff - (int)(top[i] & 0xffffu);
+    a.topk_w[t * a.top_k + i] = to_bf16_bits(ex[i] / sum);
+  }
 }
 
 }  // namespace
 
+template <int L>
+static hipError_t launch_lanes(const MoeArgs& a, hipStream_t stream) {
+  const int per_block = 4 * (64 / L);                       // tokens per workgroup of four waves
+  const dim3 grid((unsigned)((a.num_tokens + per_block - 1) / per_block)), block(256);
+  if (a.top_k <= 1) hipLaunchKernelGGL((moe_topk_softmax_kernel<1, L>), grid, block, 0, stream, a);
+  else if (a.top_k <= 2) hipLaunchKernelGGL((moe_topk_softmax_kernel<2, L>), grid, block, 0, stream, a);
+  else if (a.top_k <= 4) hipLaunchKernelGGL((moe_topk_softmax_kernel<4, L>), grid, block, 0, stream, a);
+  else hipLaunchKernelGGL((moe_topk_softmax_kernel<8, L>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream) {
   if (a.num_tokens <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((a.num_tokens + 31) / 32)), block(256);   // 32 tokens per workgroup
-  if (a.top_k <= 1) hipLaunchKernelGGL(moe_topk_softmax_kernel<1>, grid, block, 0, stream, a);
-  else if (a.top_k <= 2) hipLaunchKernelGGL(moe_topk_softmax_kernel<2>, grid, block, 0, stream, a);
-  else if (a.top_k <= 4) hipLaunchKernelGGL(moe_topk_softmax_kernel<4>, grid, block, 0, stream, a);
-  else hipLaunchKernelGGL(moe_topk_softmax_kernel<8>, grid, block, 0, stream, a);
-  return hipGetLastError();
+  // four lanes per token (one exchange level fewer) while a lane's share
+  // stays whole 16-byte chunks within the register budget, else eight
+  if (a.num_experts % 32 == 0 && a.num_experts <= 256) return launch_lanes<4>(a, stream);
+  return launch_lanes<8>(a, stream);
 }
 
 }  // namespace sinkattn

@@ -46,7 +46,8 @@ def _check(bits, k, what):
     assert (err <= 2.0 ** -8 * np.abs(rw) + 1e-6).all(), f"{what}: weights off by {err.max():.3e}"
 
 
-@pytest.mark.parametrize("experts,k", [(128, 4), (32, 4), (512, 8), (7, 7), (1, 1), (65, 3)])
+@pytest.mark.parametrize("experts,k", [(128, 4), (32, 4), (512, 8), (7, 7), (1, 1), (65, 3), (256, 8), (96, 2),
+                                        (288, 5)])
 def test_moe_random_logits(experts, k):
     rng = np.random.default_rng(experts * 10 + k)
     _check(wl._normal_bf16(rng, (4096, experts)), k, f"E={experts} K={k}")

@@ -7,7 +7,7 @@
 // all experts as DeepSeek-style models do, and the expert weights must be
 // computed in bfloat16 precision).
 //
-// Eight lanes per token (eight tokens per wave).  Each logit becomes a
+// L lanes per token (four up to 256 experts, else eight).  Each logit becomes a
 // 32-bit key: the bf16 bits mapped to an unsigned order (larger logit, larger
 // key; -0 and +0 the same) in the high half and the complemented expert index
 // in the low half, so one unsigned comparison orders by logit and, among equal
@@ -15,11 +15,11 @@
 // own experts in a descending register list; inserting a key costs one
 // three-input median per list entry (entry i becomes the median of the old
 // entries i - 1 and i and the key), and the map needs no compare-and-select,
-// so the loop is plain integer arithmetic.  Three exchange levels
-// (lanes 1, 2, 4 apart) merge the eight lists: the elementwise max of a list
-// and its partner's reversed list holds the top KP of both, and a bitonic
-// network sorts it.  Every lane then holds the token's top KP; lane s < K
-// writes the s-th expert and its weight, the softmax over the K selected bf16
+// so the loop is plain integer arithmetic.  log2(L) exchange levels (lanes
+// 1, 2, 4 apart) merge the L lists: the elementwise max of a list and its
+// partner's reversed list holds the top KP of both, and a bitonic network
+// sorts it.  Every lane then holds the token's top KP; lane s writes picks
+// s, s + L, ... (ids and weights), the softmax over the K selected bf16
 // logits evaluated in fp32 and rounded to bf16.
 
 #include "device_common.hpp"

@@ -20,7 +20,7 @@ import pytest
 
 import oracle
 from gqa_attention_sinks_amd import workloads as wl
-from tests._gpu import DeviceWorkload, say, to_host
+from tests._gpu import DeviceWorkload, assert_parity, oracle_full, say, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -131,6 +131,35 @@ def test_count_probe_chunk_sizes(window):
                 assert np.all(np.isneginf(got)), (b, c)
             else:
                 assert np.all(np.round(np.exp(got)) == cnt), (b, c, cnt, np.exp(got[:2]))
+
+
+def test_maximum_split_count():
+    """num_splits = 256, the library's maximum: a 4096-key request gets one
+    page per chunk and the short ones leave most chunks empty.  The count
+    probe gives every chunk's size exactly, and on random data the merged
+    output matches the oracle."""
+    lengths = np.array([1, 17, 4096, 300, 4095])
+    s = 256
+    w = wl.zero_query_probe(_decode_base(lengths, 78))
+    say("count probe, 256 chunks")
+    _, lse_part = DeviceWorkload(w).decode(s, merge=False)
+    lse_part = to_host(lse_part)
+    bounds = oracle.split_bounds_ref(lengths, s)
+    for b, n in enumerate(lengths):
+        for c in range(s):
+            cnt = max(0, min(bounds[b, c, 1], n) - bounds[b, c, 0])
+            got = lse_part[b, :, c]
+            if cnt == 0:
+                assert np.all(np.isneginf(got)), (b, c)
+            else:
+                assert np.all(np.round(np.exp(got)) == cnt), (b, c, cnt)
+    rng = np.random.default_rng(79)
+    w2 = wl.make_paged("max_splits", lengths, np.ones_like(lengths), 16, 2, rng=rng, decode=True,
+                       sink_overrides=wl.outlier_sinks)
+    say("decode parity, 256 chunks")
+    out, lse = DeviceWorkload(w2).decode(s)
+    ro, rl = oracle_full(w2, 0)
+    assert_parity(to_host(out), ro, "decode S=256", to_host(lse), rl)
 
 
 def test_page_permutation_is_bitwise_invisible():

@@ -71,11 +71,11 @@ class DeviceWorkload:
                           page_indices=self.page_indices, kv_len=self.kv_len if w.paged else None,
                           return_lse=return_lse, qo_indptr_host=w.qo_indptr if host_plan else None)
 
-    def decode(self, num_splits, window=0, merge=True, return_lse=True):
+    def decode(self, num_splits, window=0, merge=True, return_lse=True, sinks=True):
         w = self.w
         return sa.decode_paged(self.q, self.k, self.v, self.kv_indptr, self.page_indices, self.kv_len,
-                               self.sinks, w.scale, num_splits=num_splits, window=window, merge=merge,
-                               return_lse=return_lse)
+                               self.sinks if sinks else None, w.scale, num_splits=num_splits, window=window,
+                               merge=merge, return_lse=return_lse)
 
 
     def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True, masks=None):

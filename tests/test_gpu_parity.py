@@ -153,6 +153,22 @@ def test_decode_edge_lengths_windows(length, window):
         assert_parity(to_host(out), ro, f"decode L={length} W={window} S={s}", to_host(lse), rl)
 
 
+@pytest.mark.parametrize("heads", [(4, 4), (4, 2), (16, 1)])
+def test_decode_group_sizes_and_no_sinks(heads):
+    """GQA groups of 1, 2 and 16 query heads per KV head (the MFMA columns a
+    page load serves), with and without sinks."""
+    hq, hkv = heads
+    rng = np.random.default_rng(17 + hq * 4 + hkv)
+    w = wl.make_paged("groups", [1, 40, 700, 16], [1, 1, 1, 1], hq, hkv, rng=rng, decode=True)
+    say(f"decode group={hq // hkv}")
+    d = DeviceWorkload(w)
+    for sinks in [True, False]:
+        ro, rl = oracle_full(w, 0, sinks=sinks)
+        for s in [1, 3]:
+            out, lse = d.decode(s, sinks=sinks)
+            assert_parity(to_host(out), ro, f"decode group {hq // hkv} S={s} sinks={sinks}", to_host(lse), rl)
+
+
 def test_decode_partials_sink_only_in_chunk_zero():
     """The partials themselves: chunk 0 carries the sink, the others do not."""
     w = wl.paged_decode(batch=6, max_len=700)

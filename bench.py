@@ -192,8 +192,10 @@ def time_verify(w, args, torch, dev):
     lib = sa.load_library()
     base = Dev(w, torch, dev)
     reps = [base] + [base.replica() for _ in range(max(0, args.replicas - 1))]
-    s = args.splits if args.splits > 0 else sa.pick_num_splits(w.kv_len, w.num_kv_heads)
-    B, H, HKV, R = w.batch, w.num_qo_heads, w.num_kv_heads, int(w.meta["max_rows"])
+    R = int(w.meta["max_rows"])
+    s = args.splits if args.splits > 0 else sa.pick_num_splits_multi(w.kv_len, w.num_qo_heads, w.num_kv_heads, R,
+                                                                     with_mask="masks" in w.meta)
+    B, H, HKV = w.batch, w.num_qo_heads, w.num_kv_heads
     TQ = int(w.qo_indptr[-1])
     outs = [torch.empty_like(r.q) for r in reps]
     o_part = torch.empty((TQ, H, s, 64), dtype=torch.float32, device=dev)

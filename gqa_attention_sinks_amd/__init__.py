@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     merge,
     moe_topk_softmax,
     pick_num_splits,
+    pick_num_splits_multi,
     prefill,
     split_bounds,
 )

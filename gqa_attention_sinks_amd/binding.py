@@ -32,6 +32,7 @@ EXPORTED = (
     "sinkattn_merge",
     "sinkattn_split_bounds",
     "sinkattn_pick_num_splits",
+    "sinkattn_pick_num_splits_multi",
     "sinkattn_status_string",
     "sinkattn_last_error",
     "sinkattn_abi_version",
@@ -93,6 +94,8 @@ def load_library():
     lib.sinkattn_split_bounds.restype = i32
     lib.sinkattn_pick_num_splits.argtypes = [vp, i32, i32]
     lib.sinkattn_pick_num_splits.restype = i32
+    lib.sinkattn_pick_num_splits_multi.argtypes = [vp, i32, i32, i32, i32, i32]
+    lib.sinkattn_pick_num_splits_multi.restype = i32
     lib.sinkattn_status_string.argtypes = [i32]
     lib.sinkattn_status_string.restype = ctypes.c_char_p
     lib.sinkattn_last_error.argtypes = []
@@ -415,6 +418,15 @@ def pick_num_splits(kv_len_host, num_kv_heads: int) -> int:
     lens = np.ascontiguousarray(kv_len_host, dtype=np.int32)
     return int(load_library().sinkattn_pick_num_splits(lens.ctypes.data_as(ctypes.c_void_p), len(lens),
                                                        num_kv_heads))
+
+
+def pick_num_splits_multi(kv_len_host, num_qo_heads: int, num_kv_heads: int, max_qo_len: int,
+                          with_mask: bool = False) -> int:
+    """Host-only split count suggested for a several-row (verify) batch."""
+    lens = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    return int(load_library().sinkattn_pick_num_splits_multi(lens.ctypes.data_as(ctypes.c_void_p), len(lens),
+                                                             num_qo_heads, num_kv_heads, max_qo_len,
+                                                             int(bool(with_mask))))
 
 
 def raw_library():

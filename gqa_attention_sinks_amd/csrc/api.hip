@@ -379,6 +379,31 @@ int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int3
   return (int32_t)s;
 }
 
+int32_t sinkattn_pick_num_splits_multi(const int32_t* kv_len_host, int32_t batch, int32_t num_qo_heads,
+                                       int32_t num_kv_heads, int32_t max_qo_len, int32_t with_mask) {
+  if (kv_len_host == nullptr || batch < 1 || num_kv_heads < 1 || num_qo_heads < num_kv_heads ||
+      max_qo_len < 1)
+    return 1;
+  int64_t max_len = 0;
+  for (int32_t b = 0; b < batch; ++b) max_len = kv_len_host[b] > max_len ? kv_len_host[b] : max_len;
+  const int64_t max_pages = (max_len + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE;
+  // The several-row kernel holds one workgroup per CU for each wave it keeps
+  // per SIMD: 6, 4 or 3 for one, two or four 16-column blocks.  Aim for about
+  // 4/3 of the resident workgroups (twice with a mask, whose pages cost more)
+  // so that one round plus a short tail covers the batch: fewer, longer
+  // chunks than the one-row rule, which measured best on the verify batch.
+  const int64_t cols = (int64_t)(num_qo_heads / num_kv_heads) * max_qo_len;
+  const int64_t per_cu = cols <= 16 ? 6 : cols <= 32 ? 4 : 3;
+  const int64_t target = 256 * per_cu * (with_mask ? 2 : 4) / (with_mask ? 1 : 3);
+  const int64_t units = (int64_t)batch * num_kv_heads;
+  int64_t s = (target + units - 1) / units;
+  const int64_t cap = max_pages / 16 > 1 ? max_pages / 16 : 1;
+  if (s > cap) s = cap;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  return (int32_t)s;
+}
+
 const char* sinkattn_status_string(sinkattn_status status) {
   switch (status) {
     case SINKATTN_OK: return "ok";

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 5
+#define SINKATTN_ABI_VERSION 6
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
@@ -273,6 +273,15 @@ sinkattn_status sinkattn_split_bounds(const int32_t* kv_len_host, int32_t batch,
  * (kv_len_host [batch], host): enough (request, KV head, chunk) work units to
  * fill the GPU without making chunks shorter than a few pages. */
 int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int32_t num_kv_heads);
+
+/* Host-only: a split count for sinkattn_decode_paged_multi (kv_len_host
+ * [batch], host; max_qo_len and with_mask as in the call).  That kernel keeps
+ * fewer waves per SIMD the more (row, head) columns a KV head has, so it is
+ * given fewer, longer chunks than the one-row rule gives: about 4/3 of the
+ * workgroups the GPU holds at once (twice that with a mask), chunks of at
+ * least 16 pages, at most 16 of them.  Returns 1 on invalid arguments. */
+int32_t sinkattn_pick_num_splits_multi(const int32_t* kv_len_host, int32_t batch, int32_t num_qo_heads,
+                                       int32_t num_kv_heads, int32_t max_qo_len, int32_t with_mask);
 
 const char* sinkattn_status_string(sinkattn_status status);
 const char* sinkattn_last_error(void); /* message of this thread's last failing call */

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 5
+    assert sa.abi_version() == 6
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -69,6 +69,18 @@ def test_pick_num_splits_is_in_range(lib):
     assert 1 <= sa.pick_num_splits(np.full(64, 4096), 8) <= 256
     assert sa.pick_num_splits(np.full(8, 131072), 8) == 16
     assert sa.pick_num_splits(np.full(4, 10), 8) == 1
+
+
+def test_pick_num_splits_multi(lib):
+    lens = np.full(64, 4096)
+    # four column blocks (8 heads x 8 rows): three workgroups per CU -> about
+    # 1024 units without a mask, 1536 with one, over 512 (request, KV head) pairs
+    assert sa.pick_num_splits_multi(lens, 64, 8, 8) == 2
+    assert sa.pick_num_splits_multi(lens, 64, 8, 8, with_mask=True) == 3
+    assert sa.pick_num_splits_multi(lens, 64, 8, 2) == 4          # one block: six per CU, 2048 units
+    assert sa.pick_num_splits_multi(np.full(4, 10), 64, 8, 8) == 1   # chunks of at least 16 pages
+    assert sa.pick_num_splits_multi(np.full(2, 1 << 20), 64, 8, 8) == 16
+    assert lib.sinkattn_pick_num_splits_multi(None, 4, 64, 8, 8, 0) == 1
 
 
 # ---------------------------------------------------------------------------

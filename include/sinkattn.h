@@ -161,8 +161,10 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
  * GPT-OSS > Sink attention").  One workgroup per (request, KV head, chunk)
  * reads each page once for all G = Hq/Hkv heads and all rows of the request.
  *   q          [total_q, Hq, 64] bf16
- *   qo_indptr  [batch+1] int32 (device); every request has 1 .. max_qo_len
- *              rows (rows past max_qo_len are neither read nor written)
+ *   qo_indptr  [batch+1] int32 (device); every request must have at most
+ *              max_qo_len rows (not checked: the offsets are device memory;
+ *              the results of a request with more are undefined); a request
+ *              with no row is skipped
  *   custom_mask optional (device, NULL = the causal rule above): a draft
  *              tree verified in one step (tree attention, "Accelerating
  *              Sonar through speculation", section "Speculative decoding":

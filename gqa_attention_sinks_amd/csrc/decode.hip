@@ -361,6 +361,14 @@ void decode_paged_kernel(DecodeArgs a) {
       const int key0 = p * kPageSize + 4 * grp;
       // uniform: every key of the page visible to every column (no per-key test)
       const bool page_full = !MASK && p * kPageSize >= full_lo && p * kPageSize + kPageSize - 1 <= full_hi;
+      // with a mask: the page inside the chunk and every key visible to every
+      // real column of the block (a draft tree shows its rows the whole
+      // context, so this is every page but the last few)
+      const bool page_in = MASK && p * kPageSize >= t_lo && p * kPageSize + kPageSize - 1 <= t_hi - 1;
+      auto block_full = [&](int nb) -> bool {
+        if constexpr (!MASK) return page_full;
+        return page_in && __builtin_amdgcn_ballot_w64(c_bit[nb] >= 0 && mcur[nb] != 0xFu) == 0;
+      };
       f16x4 pb[NB];
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
@@ -386,7 +394,7 @@ void decode_paged_kernel(DecodeArgs a) {
           // column maxima, rescale, and redo the weights.
 #pragma unroll
           for (int i = 0; i < 4; ++i) pw[i] = exp2_hw(__builtin_fmaf(sc[nb][i], a.scale_log2, -m[nb]));
-          if (!page_full) {   // uniform: one branch per block, selects inside
+          if (!block_full(nb)) {   // uniform: one branch per block, selects inside
 #pragma unroll
             for (int i = 0; i < 4; ++i) pw[i] = visible(i) ? pw[i] : 0.f;
           }

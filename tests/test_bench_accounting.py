@@ -1,0 +1,78 @@
+"""The benchmark's algorithmic work, against brute-force counts (CPU only).
+
+The roofline figures divide these counts by measured kernel times, so they
+are pinned here independently of the formulas in bench.py:
+  * decode bytes: every live key's K and V row once per KV head (head_dim
+    bf16 values each), every query row's Q and output (bf16), and the int32
+    page ids plus the two per-request metadata arrays;
+  * prefill flops: 4 * head_dim per visible (query, key, head), where row t of
+    a request with n_q rows over n_k keys sits at n_k - n_q + t and sees the
+    keys at or before it (and, with a window W, its last W positions).
+"""
+
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+from gqa_attention_sinks_amd import workloads as wl
+
+
+def _decode_bytes_brute(w):
+    total = 0
+    for b in range(w.batch):
+        for _key in range(int(w.kv_len[b])):
+            for _g in range(w.num_kv_heads):
+                total += 2 * w.head_dim * 2          # one K row and one V row, bf16
+    rows = int(w.qo_indptr[-1])
+    total += rows * w.num_qo_heads * w.head_dim * 2   # Q
+    total += rows * w.num_qo_heads * w.head_dim * 2   # output
+    total += 4 * len(w.page_indices)                  # page ids
+    total += 4 * (w.batch + 1) + 4 * w.batch          # page offsets and KV lengths
+    return total
+
+
+def _prefill_flops_brute(w, window):
+    visible = 0
+    for b in range(w.batch):
+        n_q, n_k = int(w.qo_len[b]), int(w.kv_len[b])
+        for t in range(n_q):
+            pos = n_k - n_q + t
+            for j in range(n_k):
+                if j <= pos and (window == 0 or j > pos - window):
+                    visible += 1
+    return 4 * w.head_dim * visible * w.num_qo_heads
+
+
+def test_decode_bytes_small_batch():
+    w = wl.paged_decode(seed=4, batch=5, max_len=300, num_qo_heads=8, num_kv_heads=2)
+    assert bench.decode_bytes(w) == _decode_bytes_brute(w)
+
+
+def test_decode_bytes_several_rows():
+    w = wl.verify_decode(seed=2, batch=4, max_len=200, num_qo_heads=16, num_kv_heads=2)
+    assert bench.decode_bytes(w) == _decode_bytes_brute(w)
+
+
+def test_headline_decode_bytes():
+    """The figure the profiles and the benchmark line quote."""
+    assert bench.decode_bytes(wl.paged_decode()) == 274_846_980
+
+
+def test_prefill_flops_causal_and_window():
+    w = wl.make_contiguous("acct", [70, 33, 5], [70, 20, 5], 8, 2, rng=np.random.default_rng(3))
+    for window in (0, 1, 16, 128):
+        assert bench.prefill_flops(w, window) == _prefill_flops_brute(w, window), window
+
+
+def test_headline_prefill_flops():
+    """4 x 8192 causal rows, 64 heads: 4 * 64 * 64 * 4 * (8192 * 8193 / 2)."""
+    assert bench.prefill_flops(wl.causal_prefill()) == 4 * 64 * 64 * 4 * (8192 * 8193 // 2)
+
+
+def test_more_than_one_gpu_is_refused():
+    p = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert p.returncode == 2
+    assert "one GPU" in p.stderr

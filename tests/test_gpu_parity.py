@@ -140,8 +140,11 @@ def test_paged_decode_full(num_splits):
 
 
 @pytest.mark.parametrize("length", [1, 15, 16, 17, 4095, 4096])
-@pytest.mark.parametrize("window", [0, 1, 127, 128, 129])
+@pytest.mark.parametrize("window", [0, 1, 127, 128, 129, 3000])
 def test_decode_edge_lengths_windows(length, window):
+    """Lengths around a page and near the largest, windows around 128; the
+    kernel ranks requests by length unless a window of at most 2048 keys
+    makes their work alike (3000: ranked and windowed)."""
     rng = np.random.default_rng(length * 7 + window)
     w = wl.make_paged("edge", [length, max(1, length // 2)], [1, 1], 16, 2, rng=rng, decode=True,
                       sink_overrides=wl.outlier_sinks)

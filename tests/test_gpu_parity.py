@@ -298,7 +298,7 @@ def test_verify_decode_full(num_splits):
 
 
 @pytest.mark.parametrize("heads,max_rows", [((64, 8), 2), ((4, 1), 8), ((16, 1), 4), ((64, 8), 5)])
-@pytest.mark.parametrize("window", [0, 1, 3, 128])
+@pytest.mark.parametrize("window", [0, 1, 3, 128, 3000])
 def test_verify_decode_shapes_windows(heads, max_rows, window):
     hq, hkv = heads
     rng = np.random.default_rng(hq * 100 + max_rows * 10 + window)

@@ -2,7 +2,8 @@
 allocate nothing, never synchronise the host and keep no device state
 between calls.  Capture split decode + merge, prefill and a verify call
 into one graph, replay it several times with eager work in between, and
-check every replay against the eager results bit for bit."""
+check every replay against the eager results bit for bit; the same for the
+append with rotary embedding and the MoE routing."""
 
 import numpy as np
 import pytest
@@ -68,3 +69,56 @@ def test_graph_replay_matches_eager():
         for k, v in outs.items():
             assert torch.equal(v, eager[k]), f"replay {rep}: {k} differs from the eager result"
     say("graph replays match eager results")
+
+
+def test_graph_replay_append_and_moe():
+    """The append with rotary embedding and the MoE routing (both timed by
+    graph replay in the benchmark), captured together and replayed with
+    their outputs cleared and the pools restored between replays."""
+    import torch
+    import gqa_attention_sinks_amd as sa
+    from tests._gpu import bits_to_dev, i32_to_dev
+    from tests.test_gpu_append import _case
+    c = _case(61, [40, 300, 17, 1000], [5, 64, 17, 1], 16, 2)
+    q, k, v = bits_to_dev(c["q"]), bits_to_dev(c["k"]), bits_to_dev(c["v"])
+    kp0, vp0 = bits_to_dev(c["k_pool"]), bits_to_dev(c["v_pool"])
+    kp, vp = kp0.clone(), vp0.clone()
+    meta = [i32_to_dev(c[n]) for n in ("append_indptr", "page_indptr", "page_indices", "kv_len")]
+    table = torch.from_numpy(c["table"]).to("cuda:0")
+    q_out = torch.empty_like(q)
+    logits = bits_to_dev(wl._normal_bf16(np.random.default_rng(62), (777, 96)))
+    idx = torch.empty((777, 4), dtype=torch.int32, device="cuda:0")
+    wts = torch.empty((777, 4), dtype=torch.bfloat16, device="cuda:0")
+
+    def work(stream=None):
+        sa.append_paged_kv_rope(k, v, meta[0], kp, vp, meta[1], meta[2], meta[3], table, q=q, q_out=q_out,
+                                stream=stream)
+        sa.moe_topk_softmax(logits, 4, idx, wts, stream=stream)
+
+    def reset():                          # eager work between replays
+        kp.copy_(kp0)
+        vp.copy_(vp0)
+        for t in (q_out, idx, wts):
+            t.zero_()
+
+    work()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in (kp, vp, q_out, idx, wts)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        work(side)
+        side.synchronize()
+        with torch.cuda.graph(graph, stream=side):
+            work(side)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, got, ref in zip(("k_pool", "v_pool", "q_out", "topk_idx", "topk_w"),
+                                  (kp, vp, q_out, idx, wts), eager):
+            assert torch.equal(got, ref), f"replay {rep}: {name} differs from the eager result"
+    say("append and MoE graph replays match eager results")

@@ -23,4 +23,5 @@ from .binding import (  # noqa: F401
     pick_num_splits_multi,
     prefill,
     split_bounds,
+    validate_kv_host,
 )

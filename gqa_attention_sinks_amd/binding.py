@@ -33,8 +33,10 @@ EXPORTED = (
     "sinkattn_split_bounds",
     "sinkattn_pick_num_splits",
     "sinkattn_pick_num_splits_multi",
+    "sinkattn_validate_kv_host",
     "sinkattn_status_string",
     "sinkattn_last_error",
+    "sinkattn_last_hip_error",
     "sinkattn_abi_version",
 )
 
@@ -56,6 +58,7 @@ class _KV(ctypes.Structure):
         ("kv_indptr", ctypes.c_void_p),
         ("page_indices", ctypes.c_void_p),
         ("kv_len", ctypes.c_void_p),
+        ("num_pages", ctypes.c_int64),
     ]
 
 
@@ -96,10 +99,14 @@ def load_library():
     lib.sinkattn_pick_num_splits.restype = i32
     lib.sinkattn_pick_num_splits_multi.argtypes = [vp, i32, i32, i32, i32, i32]
     lib.sinkattn_pick_num_splits_multi.restype = i32
+    lib.sinkattn_validate_kv_host.argtypes = [ctypes.POINTER(_KV), vp, vp, vp, i32]
+    lib.sinkattn_validate_kv_host.restype = i32
     lib.sinkattn_status_string.argtypes = [i32]
     lib.sinkattn_status_string.restype = ctypes.c_char_p
     lib.sinkattn_last_error.argtypes = []
     lib.sinkattn_last_error.restype = ctypes.c_char_p
+    lib.sinkattn_last_hip_error.argtypes = []
+    lib.sinkattn_last_hip_error.restype = ctypes.c_char_p
     lib.sinkattn_abi_version.argtypes = []
     lib.sinkattn_abi_version.restype = i32
     _LIB = lib
@@ -166,7 +173,8 @@ def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
     elif k.dim() != 3 or k.shape[2] != HEAD_DIM:
         raise ValueError("contiguous k/v must be [total_kv, Hkv, 64]")
     return _KV(k.data_ptr(), v.data_ptr(), int(paged), PAGE_SIZE, kv_indptr.data_ptr(),
-               page_indices.data_ptr() if paged else None, kv_len.data_ptr() if paged else None)
+               page_indices.data_ptr() if paged else None, kv_len.data_ptr() if paged else None,
+               int(k.shape[0]))
 
 
 # --------------------------------------------------------------------------
@@ -427,6 +435,30 @@ def pick_num_splits_multi(kv_len_host, num_qo_heads: int, num_kv_heads: int, max
     return int(load_library().sinkattn_pick_num_splits_multi(lens.ctypes.data_as(ctypes.c_void_p), len(lens),
                                                              num_qo_heads, num_kv_heads, max_qo_len,
                                                              int(bool(with_mask))))
+
+
+def validate_kv_host(kv_indptr, num_pages: int, page_indices=None, kv_len=None):
+    """Host-only check of a batch's KV metadata (``sinkattn_validate_kv_host``)
+    before it is copied to the GPU: ``kv_indptr`` [B+1], and for a paged cache
+    ``page_indices`` and ``kv_len`` [B] (host arrays); ``num_pages`` is the
+    pool's page count (paged) or the rows of k and v (contiguous).  Raises
+    ``SinkAttnError`` naming the first bad entry."""
+    indptr = np.ascontiguousarray(kv_indptr, dtype=np.int32)
+    paged = page_indices is not None
+    pages = np.ascontiguousarray(page_indices if paged else np.zeros(1), dtype=np.int32)
+    lens = np.ascontiguousarray(kv_len if paged else np.zeros(1), dtype=np.int32)
+    if indptr.ndim != 1 or indptr.size < 1:
+        raise ValueError("kv_indptr must be a 1-D array of batch + 1 offsets")
+    if paged and lens.shape != (indptr.size - 1,):
+        raise ValueError("kv_len must have one entry per request")
+    if paged and not (0 <= int(indptr[-1]) <= pages.size):
+        raise ValueError("page_indices must hold kv_indptr[-1] entries")
+    kv = _KV(None, None, int(paged), PAGE_SIZE, None, None, None, int(num_pages))
+    vp = ctypes.c_void_p
+    _check(load_library().sinkattn_validate_kv_host(ctypes.byref(kv), indptr.ctypes.data_as(vp),
+                                                    pages.ctypes.data_as(vp) if paged else None,
+                                                    lens.ctypes.data_as(vp) if paged else None,
+                                                    indptr.size - 1))
 
 
 def raw_library():

@@ -416,6 +416,49 @@ const char* sinkattn_status_string(sinkattn_status status) {
 
 const char* sinkattn_last_error(void) { return g_last_error.c_str(); }
 
+const char* sinkattn_last_hip_error(void) { return g_last_error.c_str(); }
+
+sinkattn_status sinkattn_validate_kv_host(const sinkattn_kv* kv, const int32_t* kv_indptr_host,
+                                          const int32_t* page_indices_host,
+                                          const int32_t* kv_len_host, int32_t batch) {
+  REQUIRE(kv != nullptr && kv_indptr_host != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "kv and kv_indptr_host are required");
+  REQUIRE(batch >= 0, SINKATTN_ERR_INVALID_ARG, "batch must be >= 0 (got %d)", batch);
+  REQUIRE(kv->paged == 0 || kv->paged == 1, SINKATTN_ERR_INVALID_ARG, "kv->paged must be 0 or 1");
+  REQUIRE(kv->num_pages >= 0, SINKATTN_ERR_INVALID_ARG, "kv->num_pages must be >= 0");
+  REQUIRE(kv_indptr_host[0] >= 0, SINKATTN_ERR_INVALID_ARG, "kv_indptr[0] = %d < 0", kv_indptr_host[0]);
+  for (int32_t b = 0; b < batch; ++b)
+    REQUIRE(kv_indptr_host[b + 1] >= kv_indptr_host[b], SINKATTN_ERR_INVALID_ARG,
+            "kv_indptr decreases at request %d (%d -> %d)", b, kv_indptr_host[b], kv_indptr_host[b + 1]);
+  if (!kv->paged) {
+    REQUIRE(kv_indptr_host[batch] <= kv->num_pages, SINKATTN_ERR_INVALID_ARG,
+            "kv_indptr[%d] = %d exceeds the %lld rows of k and v", batch, kv_indptr_host[batch],
+            (long long)kv->num_pages);
+    return SINKATTN_OK;
+  }
+  REQUIRE(kv->page_size == SINKATTN_PAGE_SIZE, SINKATTN_ERR_UNSUPPORTED, "page_size %d unsupported (only 16)",
+          kv->page_size);
+  REQUIRE(kv->num_pages >= 1, SINKATTN_ERR_INVALID_ARG, "a paged pool needs num_pages >= 1");
+  REQUIRE(kv_len_host != nullptr && (page_indices_host != nullptr || kv_indptr_host[batch] == kv_indptr_host[0]),
+          SINKATTN_ERR_INVALID_ARG, "paged metadata needs kv_len_host and page_indices_host");
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = kv_len_host[b];
+    REQUIRE(len >= 0, SINKATTN_ERR_INVALID_ARG, "kv_len[%d] = %lld < 0", b, (long long)len);
+    const int64_t need = (len + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE;
+    const int64_t have = (int64_t)kv_indptr_host[b + 1] - kv_indptr_host[b];
+    REQUIRE(need <= have, SINKATTN_ERR_INVALID_ARG,
+            "request %d holds %lld keys in %lld pages but lists %lld", b, (long long)len, (long long)need,
+            (long long)have);
+    for (int64_t i = 0; i < need; ++i) {
+      const int64_t id = page_indices_host[kv_indptr_host[b] + i];
+      REQUIRE(id >= 0 && id < kv->num_pages, SINKATTN_ERR_INVALID_ARG,
+              "request %d, page %lld: id %lld outside [0, %lld)", b, (long long)i, (long long)id,
+              (long long)kv->num_pages);
+    }
+  }
+  return SINKATTN_OK;
+}
+
 int32_t sinkattn_abi_version(void) { return SINKATTN_ABI_VERSION; }
 
 }  // extern "C"

@@ -31,9 +31,6 @@
 //   columns are (row, head) pairs, up to four 16-column blocks that share
 //   every page load, each column masked at its own causal position.
 
-#include <stdio.h>
-#include <stdlib.h>
-
 #include "device_common.hpp"
 #include "kernel_args.hpp"
 
@@ -618,34 +615,15 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
 
 }  // namespace
 
-// Launch shapes: (waves per workgroup, pages in flight per wave).
-// SINKATTN_DECODE_SHAPE ("4x2", "8x1", ...) overrides the default for tuning
-// runs.
-struct DecodeShape { int nw, pf; };
-
-static DecodeShape decode_shape() {
-  static const DecodeShape shape = [] {
-    DecodeShape d{4, 1};
-    if (const char* e = getenv("SINKATTN_DECODE_SHAPE")) {
-      int nw = 0, pf = 0;
-      if (sscanf(e, "%dx%d", &nw, &pf) == 2) d = DecodeShape{nw, pf};
-    }
-    return d;
-  }();
-  return shape;
-}
-
-template <int NW, int PF>
-static void launch_shape(const DecodeArgs& a, long units, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_paged_kernel<NW, PF, 1, false, false>), dim3((unsigned)units), dim3(NW * 64), 0, stream, a);
-}
-
+// One-row decode: four waves per workgroup, one page in flight per wave (the
+// launch shape measured fastest; deeper rings of pages in flight and eight
+// waves per workgroup ran slower).
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const long units = (long)a.batch * a.num_kv_heads * a.num_splits;
   if (units <= 0) return hipSuccess;
+  const dim3 grid((unsigned)units), block(4 * 64);
   if (a.max_rows > 0) {   // several query rows per request
     const int cols = a.group * a.max_rows;
-    const dim3 grid((unsigned)units), block(4 * 64);
     if (a.custom_mask != nullptr) {
       if (cols <= 16) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, true, true>), grid, block, 0, stream, a);
       else if (cols <= 32) hipLaunchKernelGGL((decode_paged_kernel<4, 1, 2, true, true>), grid, block, 0, stream, a);
@@ -657,14 +635,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     return hipGetLastError();
   }
-  const DecodeShape d = decode_shape();
-  if (d.nw == 4 && d.pf == 1) launch_shape<4, 1>(a, units, stream);
-  else if (d.nw == 4 && d.pf == 3) launch_shape<4, 3>(a, units, stream);
-  else if (d.nw == 4 && d.pf == 4) launch_shape<4, 4>(a, units, stream);
-  else if (d.nw == 8 && d.pf == 1) launch_shape<8, 1>(a, units, stream);
-  else if (d.nw == 8 && d.pf == 2) launch_shape<8, 2>(a, units, stream);
-  else if (d.nw == 2 && d.pf == 4) launch_shape<2, 4>(a, units, stream);
-  else launch_shape<4, 2>(a, units, stream);
+  hipLaunchKernelGGL((decode_paged_kernel<4, 1, 1, false, false>), grid, block, 0, stream, a);
   return hipGetLastError();
 }
 

@@ -41,12 +41,26 @@
  *  - Errors: argument problems are found on the host before anything is
  *    enqueued, so a non-OK status means nothing was launched and nothing was
  *    written.  SINKATTN_ERR_HIP reports a failed launch.  Device-resident
- *    metadata (kv_len, page ids, index pointers) is trusted: it is not
- *    validated, since that would need a host synchronisation.
+ *    metadata (kv_len, page ids, index pointers) is trusted by the attention
+ *    calls: checking it there would need a host synchronisation.  A caller
+ *    that builds the metadata on the CPU (the usual case) checks its host
+ *    copy with sinkattn_validate_kv_host before copying it to the GPU.
  *  - Thread safety: entry points may be called concurrently from several
  *    host threads; sinkattn_last_error() is per thread.
  *  - Supported shapes: head_dim 64, page_size 16, 1 <= Hq/Hkv <= 16,
  *    Hq % Hkv == 0.
+ *  - Value range (precondition of sinkattn_prefill, sinkattn_decode_paged
+ *    and sinkattn_decode_paged_multi): the P.V products run on fp16 matrix
+ *    instructions (fp16 weights carry three more significand bits than
+ *    bf16), so V is converted from bf16 to fp16 when it is staged.  Every V
+ *    value of every key a request holds (logical keys 0 .. n_k - 1, also
+ *    those a mask or window hides: whole pages and tiles are staged) must
+ *    satisfy |v| <= 65280, the largest bf16 magnitude below fp16's overflow
+ *    at 65520.  All such values convert exactly, except magnitudes below
+ *    2^-14, which become fp16 subnormals (absolute change below 2^-24).  A
+ *    larger |v| is not detected: the output of the affected rows is
+ *    undefined (inf or NaN).  Q and K have no such limit (their products run
+ *    in bf16), and neither do the sinks.
  */
 #ifndef SINKATTN_H_
 #define SINKATTN_H_
@@ -57,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 6
+#define SINKATTN_ABI_VERSION 7
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
@@ -84,7 +98,11 @@ typedef enum {
  *                page_indices[kv_indptr[b] + j / 16]; n_k = kv_len[b].
  *                Slots past a request's last key are never read.
  *   kv_indptr [B+1] int32 and kv_len [B] int32 are device arrays; page ids are
- *   int32 but byte offsets into the pools are computed in 64 bits. */
+ *   int32 but byte offsets into the pools are computed in 64 bits.
+ *   num_pages: the capacity of k and v -- paged: pages in each pool;
+ *   contiguous: rows of k and v.  The attention calls do not read it (the
+ *   metadata is device memory); sinkattn_validate_kv_host checks a host copy
+ *   of the metadata against it. */
 typedef struct sinkattn_kv {
   const void* k;
   const void* v;
@@ -93,6 +111,7 @@ typedef struct sinkattn_kv {
   const int32_t* kv_indptr;
   const int32_t* page_indices;   /* paged only */
   const int32_t* kv_len;         /* paged only */
+  int64_t num_pages;             /* capacity of k and v (pages, or rows when contiguous) */
 } sinkattn_kv;
 
 /* Causal or sliding-window prefill over a batch of requests, each with
@@ -253,10 +272,15 @@ sinkattn_status sinkattn_append_paged_kv_rope(const void* q, const void* k_new, 
 sinkattn_status sinkattn_moe_topk_softmax(const void* logits, int32_t num_tokens, int32_t num_experts,
                                           int32_t top_k, int32_t* topk_idx, void* topk_w, void* stream);
 
-/* Log-sum-exp merge of split partials (the combination implied by splitting
- * the softmax along the KV sequence): per (row, head), with M = max_c lse_c
- * and w_c = exp(lse_c - M), out = sum_c w_c o_c / sum_c w_c and
- * lse = M + ln sum_c w_c; all-(-inf) rows give out = 0, lse = -inf.
+/* Log-sum-exp merge of split partials: "GPT-OSS on day 0", section "Kernels
+ * for GPT-OSS > Sink attention" -- attention split into blocks along the KV
+ * sequence, the sink carried by the first block only; each block's partial
+ * is a softmax over its own keys with its own log-sum-exp, and the blocks
+ * combine into the softmax over all keys.  Per (row, head), with
+ * M = max_c lse_c and w_c = exp(lse_c - M), out = sum_c w_c o_c / sum_c w_c
+ * and lse = M + ln sum_c w_c; all-(-inf) rows give out = 0, lse = -inf.  The
+ * sink needs no argument here: it is already inside the first block's
+ * partial (its LSE includes it, its output carries no value for it).
  *   o_part [rows, num_heads, num_splits, 64] fp32, lse_part [rows, num_heads,
  *   num_splits] fp32; out [rows, num_heads, 64] bf16; lse_out optional
  *   [rows, num_heads] fp32. */
@@ -285,8 +309,29 @@ int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int3
 int32_t sinkattn_pick_num_splits_multi(const int32_t* kv_len_host, int32_t batch, int32_t num_qo_heads,
                                        int32_t num_kv_heads, int32_t max_qo_len, int32_t with_mask);
 
+/* Host-only: check a host copy of a batch's KV metadata before it is copied to
+ * the GPU ("Accelerating Sonar through speculation", section "Inference with
+ * speculative decoding": the CPU builds the page metadata that configures
+ * the attention kernel and copies it to GPU memory).  kv supplies paged,
+ * page_size and num_pages (its device pointers are not read); the three
+ * arrays are host memory: kv_indptr_host [batch+1], and when paged
+ * page_indices_host [kv_indptr_host[batch]] and kv_len_host [batch].
+ * Checks, for every request b:
+ *   paged:      0 <= kv_indptr[b] <= kv_indptr[b+1]; kv_len[b] >= 0;
+ *               ceil(kv_len[b] / 16) <= kv_indptr[b+1] - kv_indptr[b] (the
+ *               pages the attention calls read); each of those page ids in
+ *               [0, num_pages); num_pages >= 1
+ *   contiguous: 0 <= kv_indptr[b] <= kv_indptr[b+1] <= num_pages
+ * Returns SINKATTN_OK, or SINKATTN_ERR_INVALID_ARG with the first offending
+ * entry named in sinkattn_last_error().  Page ids past a request's live pages
+ * are not read by the kernels and not checked. */
+sinkattn_status sinkattn_validate_kv_host(const sinkattn_kv* kv, const int32_t* kv_indptr_host,
+                                          const int32_t* page_indices_host,
+                                          const int32_t* kv_len_host, int32_t batch);
+
 const char* sinkattn_status_string(sinkattn_status status);
 const char* sinkattn_last_error(void); /* message of this thread's last failing call */
+const char* sinkattn_last_hip_error(void); /* the same message (name kept for HIP-error callers) */
 int32_t sinkattn_abi_version(void);
 
 #ifdef __cplusplus

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 6
+    assert sa.abi_version() == 7
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
@@ -94,7 +94,7 @@ INVALID, UNSUPPORTED = 1, 2
 
 def _kv(paged=1, page_size=16, k=FAKE, page_indices=FAKE, kv_len=FAKE):
     return binding._KV(k, FAKE, paged, page_size, FAKE, page_indices if paged else None,
-                       kv_len if paged else None)
+                       kv_len if paged else None, 0)
 
 
 def _prefill(lib, kv, q=FAKE, qo=FAKE, out=FAKE, batch=2, total_q=4, hq=8, hkv=2, d=64, scale=0.125, window=0,
@@ -258,3 +258,72 @@ def test_split_bounds_argument_errors(lib):
     f = lib.sinkattn_split_bounds
     assert f(None, 1, 16, 2, out.ctypes.data_as(ctypes.c_void_p)) == INVALID
     assert f(lens.ctypes.data_as(ctypes.c_void_p), 1, 16, 0, out.ctypes.data_as(ctypes.c_void_p)) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# host validation of CPU-built KV metadata (sinkattn_validate_kv_host)
+# ---------------------------------------------------------------------------
+
+def _paged_meta():
+    from gqa_attention_sinks_amd import workloads as wl
+    rng = np.random.default_rng(5)
+    kv_len = np.array([1, 16, 17, 300, 4096])
+    return wl.make_paged("validate", kv_len, np.ones_like(kv_len), 8, 2, rng=rng)
+
+
+def test_validate_accepts_the_workload_generators(lib):
+    from gqa_attention_sinks_amd import workloads as wl
+    w = _paged_meta()
+    sa.validate_kv_host(w.kv_indptr, w.num_pages, w.page_indices, w.kv_len)
+    c = wl.make_contiguous("validate_c", [5, 9], [5, 1], 4, 1, rng=np.random.default_rng(1))
+    sa.validate_kv_host(c.kv_indptr, c.k.shape[0])
+
+
+def _expect_invalid(fn, needle):
+    with pytest.raises(sa.SinkAttnError) as e:
+        fn()
+    assert e.value.status == INVALID
+    assert needle in str(e.value), str(e.value)
+
+
+def test_validate_rejects_bad_metadata(lib):
+    w = _paged_meta()
+    ok = (w.kv_indptr, w.num_pages, w.page_indices, w.kv_len)
+    # a page id at the pool's end (one past the last page)
+    pages = w.page_indices.copy()
+    pages[int(w.kv_indptr[3]) + 5] = w.num_pages
+    _expect_invalid(lambda: sa.validate_kv_host(ok[0], ok[1], pages, ok[3]), "request 3, page 5")
+    pages[int(w.kv_indptr[3]) + 5] = -1
+    _expect_invalid(lambda: sa.validate_kv_host(ok[0], ok[1], pages, ok[3]), "outside [0,")
+    # a request longer than its page list (17 keys need 2 pages)
+    lens = w.kv_len.copy()
+    lens[1] = 17
+    _expect_invalid(lambda: sa.validate_kv_host(ok[0], ok[1], ok[2], lens), "request 1 holds 17 keys")
+    lens[1] = -1
+    _expect_invalid(lambda: sa.validate_kv_host(ok[0], ok[1], ok[2], lens), "kv_len[1]")
+    # decreasing page-list offsets
+    indptr = w.kv_indptr.copy()
+    indptr[2] = indptr[1] - 1
+    _expect_invalid(lambda: sa.validate_kv_host(indptr, ok[1], ok[2], ok[3]), "decreases at request 1")
+    # contiguous rows past the end of k and v
+    _expect_invalid(lambda: sa.validate_kv_host(np.array([0, 5, 14]), 13), "exceeds the 13 rows")
+    # an empty pool cannot hold pages
+    kv = binding._KV(None, None, 1, 16, None, None, None, 0)
+    z = np.zeros(2, dtype=np.int32)
+    assert lib.sinkattn_validate_kv_host(ctypes.byref(kv), z.ctypes.data_as(ctypes.c_void_p), None,
+                                         z.ctypes.data_as(ctypes.c_void_p), 1) == INVALID
+
+
+def test_validate_ignores_pages_past_the_live_ones(lib):
+    # the page list may be longer than the keys need; only live pages are read
+    indptr = np.array([0, 3], dtype=np.int32)
+    pages = np.array([0, 1, 99], dtype=np.int32)       # the third page is never read
+    sa.validate_kv_host(indptr, 2, pages, np.array([20]))
+    sa.validate_kv_host(np.array([0, 3, 3]), 2, pages, np.array([20, 0]))   # a request with no key
+    _expect_invalid(lambda: sa.validate_kv_host(indptr, 2, pages, np.array([33])), "id 99")
+
+
+def test_last_hip_error_is_the_last_error(lib):
+    assert _decode(lib, _kv(), s=0) == INVALID
+    assert lib.sinkattn_last_hip_error() == lib.sinkattn_last_error()
+    assert b"num_splits" in lib.sinkattn_last_hip_error()

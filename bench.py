@@ -1,26 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the sink-attention hot path on one MI355X.
 
-Default run (one JSON line on stdout):
-  * headline: paged split-KV decode, 64 requests with KV lengths uniform in
-    [1, 4096], 64 query / 8 KV heads, head_dim 64, page size 16, pages
-    permuted in a shared pool, sinks N(0, 2).  One step = one whole pass of
-    the decode path: per-(request, KV head, chunk) split decode (chunk bounds
-    computed on the device, paged gather, scores, mask, streaming softmax
-    with the sink in chunk 0, P.V, partials) followed by the LSE merge.
-    ``value`` = algorithmic HBM bytes / step time (GB/s), inputs resident in
-    HBM, three replicas of the KV pool rotated so no step finds its KV in the
-    256 MB Infinity Cache.  The K timed steps are captured in one HIP graph
-    and replayed, as a serving loop issues its decode steps; the time of the
-    same steps issued one by one is reported beside it.
-  * ``roofline``: the decode kernel alone, timed with HIP events on the
-    stream it runs on, against 8 TB/s.
-  * ``prefill``: causal prefill, 4 x 8192 tokens, 64/8 heads: TFLOP/s of
-    4 * head_dim flops per visible (query, key, head) against 2.5 PFLOP/s.
-  * ``cpu_baseline``: the fp64 oracle on the host, timed on the whole decode
-    workload, plus the parity of the timed GPU output against it.
+Default run (one JSON line on stdout), every workload at full size, inputs
+resident in HBM before any timed region:
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+  * headline (``value``): paged split-KV decode, 64 requests with KV lengths
+    uniform in [1, 4096], 64 query / 8 KV heads, head_dim 64, page size 16,
+    pages permuted in a shared pool, sinks N(0, 2).  One step = one whole pass
+    of the decode path: per-(request, KV head, chunk) split decode (chunk
+    bounds computed on the device, paged gather, scores, mask, streaming
+    softmax with the sink in chunk 0, P.V, partials) and the LSE merge.
+    ``value`` = algorithmic HBM bytes / step time (GB/s); three replicas of
+    the KV pool are rotated so that no step finds its KV in the 256 MB
+    Infinity Cache.  The K timed steps are captured in one HIP graph and
+    replayed, as a serving loop issues its decode steps; the same steps
+    issued one by one are timed beside it.
+  * ``roofline``: the decode kernel alone, each launch timed with HIP events
+    on the stream it runs on, against 8 TB/s.
+  * ``configs``: every workload -- tiny prefill, paged decode, causal
+    prefill 4 x 8192, long split decode (8 x 131072 keys, 16 chunks + merge),
+    and the mixed chunked-prefill + decode batch under a 128-key window and
+    under full causal attention (its prefill and decode kernels timed apart,
+    plus the whole call against the sum of their roofline times).  Each
+    kernel carries mean / median / p10 / p90 launch times, its algorithmic
+    work and its fraction of the roofline; each workload carries a parity
+    summary of the timed output against the fp64 oracle.
+  * ``cpu_baseline``: the fp64 oracle, as it stands, timed on the host's
+    cores in this same run (a process pool over request sub-batches, one
+    BLAS thread per process), before the GPU is touched; per workload a
+    stated sample.  Its outputs are the parity reference above.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+       python bench.py --workload NAME     (one workload only, for profiling)
 """
 
 import argparse
@@ -37,6 +48,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, vendor spec
 METRIC = "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), oracle-matched"
+ATOL, RTOL = 2e-3, 1e-2        # per element |gpu - ref| <= ATOL + RTOL * |ref|
+
+WORKLOADS = ["paged_decode", "tiny_prefill", "causal_prefill", "long_split_decode", "mixed_batch",
+             "verify_decode", "verify_tree", "append_rope", "moe_topk", "copy_calibration"]
 
 
 def log(*a):
@@ -50,15 +65,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--splits", type=int, default=0, help="decode split count (0: library's pick)")
     p.add_argument("--replicas", type=int, default=3)
-    p.add_argument("--prefill-steps", type=int, default=20)
-    p.add_argument("--no-prefill", action="store_true")
-    p.add_argument("--no-cpu", action="store_true")
-    p.add_argument("--workload", default="paged_decode",
-                   choices=["paged_decode", "long_split_decode", "causal_prefill", "mixed_batch", "tiny_prefill",
-                            "verify_decode", "verify_tree", "append_rope", "moe_topk",
-                            "copy_calibration"],
-                   help="for profiling runs: time only this workload (copy_calibration: a plain "
-                        "256 MiB device copy, the reference for HBM byte counters)")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle (no cpu_baseline, no parity)")
+    p.add_argument("--workload", default=None, choices=WORKLOADS,
+                   help="for profiling runs: time only this workload (copy_calibration: a plain 256 MiB "
+                        "device copy, the reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -66,10 +76,20 @@ def parse():
 # algorithmic work
 # ---------------------------------------------------------------------------
 
-def decode_bytes(w):
-    """K + V of every live key once per KV head, + Q + out of every query row
-    + metadata."""
-    kv = int(np.sum(w.kv_len, dtype=np.int64)) * w.num_kv_heads * w.head_dim * 2 * 2
+def visible_keys(w, window=0):
+    """Per request, the keys some query row sees: row t of a request with
+    n_q rows over n_k keys sits at n_k - n_q + t, so the union of the rows'
+    ranges holds min(n_k, n_q + W - 1) keys under a window W, n_k without."""
+    n_k = np.asarray(w.kv_len, dtype=np.int64)
+    if window <= 0:
+        return n_k
+    return np.minimum(n_k, np.diff(np.asarray(w.qo_indptr, dtype=np.int64)) + window - 1)
+
+
+def decode_bytes(w, window=0):
+    """K + V of every visible key once per KV head, + Q + out of every query
+    row + metadata."""
+    kv = int(np.sum(visible_keys(w, window))) * w.num_kv_heads * w.head_dim * 2 * 2
     qo = 2 * int(w.qo_indptr[-1]) * w.num_qo_heads * w.head_dim * 2
     meta = 4 * (len(w.page_indices) + 2 * w.batch + 1)
     return kv + qo + meta
@@ -86,11 +106,250 @@ def prefill_flops(w, window=0):
     return 4 * w.head_dim * vis * w.num_qo_heads
 
 
+def sub_batch(w, reqs):
+    """The same attention call restricted to the requests ``reqs`` (the
+    paged pool is shared, contiguous K/V rows are copied)."""
+    from gqa_attention_sinks_amd import workloads as wl
+    reqs = np.asarray(reqs, dtype=np.int64)
+    qo = np.asarray(w.qo_indptr, dtype=np.int64)
+    rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in reqs]) if len(reqs) else np.zeros(0, np.int64)
+    qo_len = qo[reqs + 1] - qo[reqs]
+    new = wl.Workload(**{**w.__dict__})
+    new.q = w.q[rows]
+    new.qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int32)
+    new.kv_len = np.asarray(w.kv_len)[reqs].astype(np.int32)
+    kvp = np.asarray(w.kv_indptr, dtype=np.int64)
+    if w.paged:
+        new.page_indices = np.concatenate([w.page_indices[kvp[b]:kvp[b + 1]] for b in reqs]).astype(np.int32)
+        n_pages = kvp[reqs + 1] - kvp[reqs]
+        new.kv_indptr = np.concatenate([[0], np.cumsum(n_pages)]).astype(np.int32)
+    else:
+        krows = np.concatenate([np.arange(kvp[b], kvp[b + 1]) for b in reqs])
+        new.k, new.v = w.k[krows], w.v[krows]
+        new.kv_indptr = np.concatenate([[0], np.cumsum(kvp[reqs + 1] - kvp[reqs])]).astype(np.int32)
+    return new
+
+
+def kv_head_group(w, g):
+    """A contiguous workload restricted to KV head g and its query heads (a
+    GQA group of one KV head)."""
+    from gqa_attention_sinks_amd import workloads as wl
+    G = w.num_qo_heads // w.num_kv_heads
+    new = wl.Workload(**{**w.__dict__})
+    new.q = np.ascontiguousarray(w.q[:, g * G:(g + 1) * G])
+    new.k = np.ascontiguousarray(w.k[:, g:g + 1])
+    new.v = np.ascontiguousarray(w.v[:, g:g + 1])
+    new.sinks = w.sinks[g * G:(g + 1) * G].copy()
+    new.num_qo_heads, new.num_kv_heads = G, 1
+    return new
+
+
+def balanced_groups(weights, n):
+    """Split request indices into n groups of about equal total weight."""
+    order = np.argsort(-np.asarray(weights, dtype=np.float64), kind="stable")
+    load = np.zeros(n)
+    groups = [[] for _ in range(n)]
+    for b in order:
+        i = int(np.argmin(load))
+        groups[i].append(int(b))
+        load[i] += weights[b]
+    return [sorted(g) for g in groups if g]
+
+
+def stats_ms(samples):
+    a = np.asarray(samples, dtype=np.float64)
+    return {"mean": round(float(a.mean()), 5), "median": round(float(np.median(a)), 5),
+            "p10": round(float(np.percentile(a, 10)), 5), "p90": round(float(np.percentile(a, 90)), 5),
+            "n": int(a.size)}
+
+
+def roofline_entry(kernel, bound, work, ms, traffic=None):
+    """Achieved rate of one kernel from its mean launch time."""
+    if bound == "hbm":
+        achieved, peak, unit = work / (ms * 1e-3) / 1e9, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = work / (ms * 1e-3) / 1e12, MFMA_PEAK_TFLOPS, "TFLOP/s"
+    return {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel}
+
+
+# ---------------------------------------------------------------------------
+# the oracle on the host (cpu_baseline): a fork-based process pool, started
+# before anything touches the GPU, each process running the unchanged oracle
+# on a sub-batch with one BLAS thread
+# ---------------------------------------------------------------------------
+
+_JOBS = {}          # job id -> (workload, window, kind); inherited by the forked workers
+
+
+def _limit_blas():
+    from threadpoolctl import threadpool_limits
+    threadpool_limits(limits=1)
+
+
+def _oracle_job(key):
+    import oracle
+    w, window, kind = _JOBS[key]
+    kv = (oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr, paged=True, page_indices=w.page_indices,
+                         kv_len=w.kv_len, page_size=w.page_size) if w.paged
+          else oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr))
+    t0 = time.perf_counter()
+    if kind == "split":
+        o_part, lse_part = oracle.split_partials_ref(w.q, kv, w.sinks, w.scale, w.num_splits, window, workers=1)
+        out, lse = oracle.merge_ref(o_part, lse_part)
+    else:
+        out, lse = oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, window, workers=1)
+    return key, out.astype(np.float32), lse.astype(np.float32), time.perf_counter() - t0
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+class OracleRuns:
+    """Runs every workload's oracle sample on the host cores and keeps the
+    outputs (fp32 copies of the fp64 results) for the parity summaries."""
+
+    def __init__(self, cores):
+        import multiprocessing as mp
+        self.cores = cores
+        self.ctx = mp.get_context("fork")
+        self.results = {}
+        self.baselines = {}
+
+    def run(self, name, jobs, work, unit, sample, min_seconds=0.0):
+        """jobs: list of (workload, window, kind, rows_or_None); the jobs run
+        together on the pool (repeated until min_seconds have passed, the
+        outputs kept from the first pass)."""
+        _JOBS.clear()
+        for i, (w, window, kind, _) in enumerate(jobs):
+            _JOBS[i] = (w, window, kind)
+        procs = min(self.cores, len(jobs))
+        passes, wall = 0, 0.0
+        with self.ctx.Pool(procs, initializer=_limit_blas) as pool:
+            while passes == 0 or wall < min_seconds:
+                t0 = time.perf_counter()
+                res = pool.map(_oracle_job, range(len(jobs)), chunksize=1)
+                wall += time.perf_counter() - t0
+                if passes == 0:
+                    self.results[name] = [(jobs[k][3], out, lse) for k, out, lse, _ in sorted(res, key=lambda r: r[0])]
+                passes += 1
+        rate = passes * work / wall / (1e12 if unit == "TFLOP/s" else 1e9)
+        self.baselines[name] = {"value": float(f"{rate:.4g}"), "unit": unit, "cores": procs, "kind": "oracle",
+                                "sample": f"{sample}; {passes} pass(es) in {wall:.1f} s on {procs} processes "
+                                          f"(fp64 numpy, one BLAS thread each)",
+                                "seconds": round(wall, 2)}
+        log(f"oracle {name}: {self.baselines[name]['value']} {unit}, {wall:.1f} s")
+
+
+def run_oracles(ws, cores):
+    """The oracle samples of every workload (and the parity references)."""
+    oc = OracleRuns(cores)
+    # tiny prefill: the whole call (one (request, KV head) unit)
+    w = ws["tiny_prefill"]
+    oc.run("tiny_prefill", [(w, 0, "attn", np.asarray([0]))], prefill_flops(w), "GFLOP/s",
+           "whole call (1 request x 1 KV head)", min_seconds=1.0)
+    # paged decode: the whole batch in balanced sub-batches of requests
+    w = ws["paged_decode"]
+    groups = balanced_groups(w.kv_len, cores)
+    jobs = [(sub_batch(w, g), 0, "attn", np.asarray(g)) for g in groups]
+    oc.run("paged_decode", jobs, decode_bytes(w), "GB/s",
+           f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys) in {len(groups)} sub-batches",
+           min_seconds=5.0)
+    # causal prefill: (request, KV head) units, one per core (at most all 32)
+    w = ws["causal_prefill"]
+    units = [(u // w.num_kv_heads, u % w.num_kv_heads) for u in range(min(cores, w.batch * w.num_kv_heads))]
+    jobs = []
+    for b, g in units:
+        jobs.append((kv_head_group(sub_batch(w, [b]), g), 0, "attn", (b, g)))
+    flops = sum(prefill_flops(j[0]) for j in jobs)
+    oc.run("causal_prefill", jobs, flops, "TFLOP/s",
+           f"{len(units)} of {w.batch * w.num_kv_heads} (request, KV head) units, every row of each "
+           f"({len(units) * (w.num_qo_heads // w.num_kv_heads)} of {w.batch * w.num_qo_heads} (request, head) "
+           f"pairs)")
+    # long split decode: each request's 16 chunk partials and their merge
+    w = ws["long_split_decode"]
+    jobs = [(sub_batch(w, [b]), 0, "split", np.asarray([b])) for b in range(w.batch)]
+    oc.run("long_split_decode", jobs, decode_bytes(w), "GB/s",
+           f"whole workload ({w.batch} requests x {int(w.kv_len[0])} keys, {w.num_splits} chunk partials "
+           f"+ merge), one request per process")
+    # mixed batch, 128-key window: the whole call
+    w = ws["mixed_batch"]
+    n_pre = int(w.meta["n_prefill"])
+    work = np.asarray(w.qo_len, dtype=np.float64) * np.minimum(np.asarray(w.kv_len), 128 + w.qo_len)
+    groups = balanced_groups(work, cores)
+    jobs = [(sub_batch(w, g), 128, "attn", np.asarray(g)) for g in groups]
+    oc.run("mixed_batch_w128", jobs, prefill_flops(w, 128), "TFLOP/s",
+           f"whole call ({w.batch} requests) in {len(groups)} sub-batches")
+    # mixed batch, full causal: every other prefill chunk, and every decode row
+    pre = list(range(0, n_pre, 2))
+    dec = list(range(n_pre, w.batch))
+    dec_groups = balanced_groups(np.asarray(w.kv_len)[dec], max(1, cores - len(pre)))
+    jobs = [(sub_batch(w, [b]), 0, "attn", np.asarray([b])) for b in pre]
+    jobs += [(sub_batch(w, [dec[i] for i in g]), 0, "attn", np.asarray([dec[i] for i in g])) for g in dec_groups]
+    sample_w = sub_batch(w, pre + dec)
+    oc.run("mixed_batch_full", jobs, prefill_flops(sample_w), "TFLOP/s",
+           f"{len(pre)} of {n_pre} prefill chunks (every other one) and all {len(dec)} decode rows")
+    return oc
+
+
+def parity_summary(g, r, lse_g=None, lse_r=None, rows=None):
+    g = np.asarray(g, dtype=np.float64)
+    r = np.asarray(r, dtype=np.float64)
+    err = np.abs(g - r)
+    big = np.abs(r) >= 1e-2
+    res = {"rows": int(g.shape[0]), "elements": int(g.size), "max_abs": float(err.max()),
+           "max_rel": float((err[big] / np.abs(r[big])).max()) if big.any() else 0.0,
+           "within_tol": bool(np.all(err <= ATOL + RTOL * np.abs(r)) and np.isfinite(g).all())}
+    if lse_g is not None:
+        lg, lr = np.asarray(lse_g, np.float64), np.asarray(lse_r, np.float64)
+        fin = np.isfinite(lr)
+        res["lse_max_abs"] = float(np.abs(lg[fin] - lr[fin]).max()) if fin.any() else 0.0
+        res["lse_inf_match"] = bool(np.array_equal(lg[~fin], lr[~fin]))
+    return res
+
+
+def parity_from_oracle(oc, name, w, out_host, lse_host):
+    """Compare the GPU output rows that the oracle sample covers."""
+    if oc is None or name not in oc.results:
+        return None
+    gs, rs, lgs, lrs = [], [], [], []
+    qo = np.asarray(w.qo_indptr, dtype=np.int64)
+    G = w.num_qo_heads // w.num_kv_heads
+    for key, out, lse in oc.results[name]:
+        if isinstance(key, tuple):                       # (request, KV head) unit
+            b, g = key
+            rows = np.arange(qo[b], qo[b + 1])
+            heads = slice(g * G, (g + 1) * G)
+            gs.append(out_host[rows][:, heads])
+            lgs.append(lse_host[rows][:, heads] if lse_host is not None else None)
+        else:                                            # whole requests
+            rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in key])
+            gs.append(out_host[rows])
+            lgs.append(lse_host[rows] if lse_host is not None else None)
+        rs.append(out)
+        lrs.append(lse)
+    flat = lambda xs: np.concatenate([x.reshape(-1, x.shape[-1]) for x in xs])
+    g, r = flat(gs), flat(rs)
+    lse_ok = all(x is not None for x in lgs)
+    lg = np.concatenate([x.reshape(-1) for x in lgs]) if lse_ok else None
+    lr = np.concatenate([x.reshape(-1) for x in lrs]) if lse_ok else None
+    return parity_summary(g, r, lg, lr)
+
+
 # ---------------------------------------------------------------------------
 # GPU runs
 # ---------------------------------------------------------------------------
 
 class Dev:
+    """A workload's inputs in device memory."""
+
     def __init__(self, w, torch, dev):
         def bits(a):
             return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -112,13 +371,29 @@ class Dev:
         return r
 
 
-def time_decode(w, args, torch, dev):
-    """Decode + merge steps through the C ABI with prebuilt arguments (the
-    Python binding's checks would otherwise cost more than a step).  The
+def launch_times(fn, n, stream, torch):
+    """n calls of fn, each between two HIP events on ``stream`` (the events
+    are recorded back to back, so call i's time is e[i+1] - e[i])."""
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    ev[0].record(stream)
+    for i in range(n):
+        fn(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+
+
+def to_host(t):
+    return t.float().cpu().numpy()
+
+
+def time_decode(w, args, torch, dev, window=0):
+    """Split decode + merge steps through the C ABI with prebuilt arguments
+    (the Python binding's checks would otherwise cost more than a step).  The
     step time is that of the K steps captured in one HIP graph and replayed
     (as a serving loop issues its decode steps); the same steps issued one by
-    one from Python are timed beside it.  The output checked against the
-    oracle is the graph replay's."""
+    one from Python are timed beside it; then each kernel is timed per launch
+    with events.  The output returned is the graph replay's."""
     import ctypes
     import gqa_attention_sinks_amd as sa
     from gqa_attention_sinks_amd import binding
@@ -130,7 +405,7 @@ def time_decode(w, args, torch, dev):
     outs = [torch.empty_like(r.q) for r in reps]
     o_part = torch.empty((B, H, s, 64), dtype=torch.float32, device=dev)
     lse_part = torch.empty((B, H, s), dtype=torch.float32, device=dev)
-    lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    lses = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in reps]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = ctypes.c_void_p
@@ -138,20 +413,31 @@ def time_decode(w, args, torch, dev):
     qp = [P(r.q.data_ptr()) for r in reps]
     sk = [P(r.sinks.data_ptr()) for r in reps]
     op = [P(o.data_ptr()) for o in outs]
-    opart, lpart, lsep = P(o_part.data_ptr()), P(lse_part.data_ptr()), P(lse.data_ptr())
+    lp = [P(x.data_ptr()) for x in lses]
+    opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
     scale = ctypes.c_float(w.scale)
 
-    def step(i, sp=sp):
-        r = i % len(reps)
-        if s > 1:
-            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
-                                           B, H, HKV, 64, scale, 0, sp)
-            st |= lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lsep, sp)
-        else:
-            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lsep,
-                                           B, H, HKV, 64, scale, 0, sp)
+    def check(st):
         if st != 0:
             raise RuntimeError(lib.sinkattn_last_error().decode())
+
+    def decode_only(i, sp=sp):
+        r = i % len(reps)
+        if s > 1:
+            check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
+                                            B, H, HKV, 64, scale, window, sp))
+        else:
+            check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lp[r],
+                                            B, H, HKV, 64, scale, window, sp))
+
+    def merge_only(i, sp=sp):
+        r = i % len(reps)
+        check(lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lp[r], sp))
+
+    def step(i, sp=sp):
+        decode_only(i, sp)
+        if s > 1:
+            merge_only(i, sp)
 
     for i in range(args.warmup):
         step(i)
@@ -181,37 +467,321 @@ def time_decode(w, args, torch, dev):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     last = (args.steps - 1) % len(reps)
-    out_host = outs[last].float().cpu().numpy().astype(np.float64)
-    # the decode kernel alone: K back-to-back launches between two events on
-    # the stream they run on (rotating the replicas), then the merge alone
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    out_host, lse_host = to_host(outs[last]), to_host(lses[last])
+    del graph
+    n = max(args.steps, 100)
+    dec = launch_times(decode_only, n, stream, torch)
+    mer = launch_times(merge_only, n, stream, torch) if s > 1 else [0.0]
+    torch.cuda.synchronize()
+    return dict(step_ms=wall * 1e3, step_ms_eager=wall_eager * 1e3, decode=dec, merge=mer, splits=s,
+                out=out_host, lse=lse_host)
+
+
+def time_prefill(w, n, warmup, torch, dev, window=0, d=None):
+    """sinkattn_prefill on a workload, each call between events; returns the
+    per-call times and the output."""
+    from gqa_attention_sinks_amd import binding
+    d = d or Dev(w, torch, dev)
+    out = torch.empty_like(d.q)
+    lse = torch.empty((w.total_q, w.num_qo_heads), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    host = np.ascontiguousarray(w.qo_indptr, dtype=np.int32)
+
+    def call(i=0):
+        binding.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale, window=window,
+                        page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out, lse=lse,
+                        qo_indptr_host=host)
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    times = launch_times(call, n, stream, torch)
+    return dict(times=times, out=to_host(out), lse=to_host(lse))
+
+
+def graph_call_ms(call, n, torch):
+    """Per-call time of a few-microsecond call: n calls captured in one HIP
+    graph and replayed (the host's launch rate does not enter)."""
+    stream = torch.cuda.current_stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    for i in range(args.steps):
-        r = i % len(reps)
-        if s > 1:
-            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
-                                           B, H, HKV, 64, scale, 0, sp)
-        else:
-            st = lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lsep,
-                                           B, H, HKV, 64, scale, 0, sp)
+    g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def measured_traffic(kernel, workload, splits):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE runs, or
+    None when the kernel's sources changed since they were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(kernel)
+    csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
+    files = [os.path.join(csrc, f) for f in ("decode.hip", "device_common.hpp", "kernel_args.hpp")]
+    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
+    if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
+            or rec.get("num_splits") != splits:
+        return None
+    return int(round(rec["bytes"]))
+
+
+# ---------------------------------------------------------------------------
+# per-workload GPU legs
+# ---------------------------------------------------------------------------
+
+DESCR = {
+    "tiny_prefill": "tiny prefill: batch 1, 4 query / 1 KV head, head_dim 64, causal 128, contiguous KV, "
+                    "sinks N(0, 1), seed 0",
+    "paged_decode": "paged decode: batch 64, one query token each, KV lengths uniform in [1, 4096], 64 query / "
+                    "8 KV heads, head_dim 64, page size 16, pages permuted in a shared pool, sinks N(0, 2), seed 0",
+    "causal_prefill": "causal prefill: batch 4 x 8192 tokens, 64 query / 8 KV heads, head_dim 64, contiguous KV, "
+                      "scale 1/8, sinks N(0, 2), full causal, seed 0",
+    "long_split_decode": "long split decode: batch 8, 131072 keys each, 64 query / 8 KV heads, paged (page 16), "
+                         "16 chunks with the sink in chunk 0 only, then the LSE merge; sinks N(0, 2) with -inf "
+                         "and +20 outliers, seed 0",
+    "mixed_batch": "mixed batch: 16 prefill chunks of 512 tokens on prefixes uniform in [0, 16384] + 240 decode "
+                   "rows with KV lengths uniform in [1, 16384] in one call, 64 query / 8 KV heads, paged "
+                   "(page 16), sinks N(0, 2), seed 0",
+}
+
+
+def leg_tiny(w, args, torch, dev, oc):
+    import gqa_attention_sinks_amd as sa
+    d = Dev(w, torch, dev)
+    r = time_prefill(w, max(args.steps, 100), args.warmup, torch, dev, d=d)
+    out = torch.empty_like(d.q)
+    host = np.ascontiguousarray(w.qo_indptr, dtype=np.int32)
+    graph_ms = graph_call_ms(lambda: sa.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale,
+                                                 out=out, qo_indptr_host=host), 100, torch)
+    flops = prefill_flops(w)
+    st = stats_ms(r["times"])
+    return {"workload": DESCR["tiny_prefill"], "bound": "latency (launch)",
+            "kernels": {"prefill_kernel": {"ms": st, "algorithmic_flops": flops,
+                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"])}},
+            "call_ms_graph_replay": round(graph_ms, 5),
+            "parity": parity_from_oracle(oc, "tiny_prefill", w, r["out"], r["lse"]),
+            "cpu_baseline": oc.baselines.get("tiny_prefill") if oc else None}
+
+
+def leg_causal_prefill(w, args, torch, dev, oc):
+    r = time_prefill(w, 30, 3, torch, dev)
+    flops = prefill_flops(w)
+    st = stats_ms(r["times"])
+    return {"workload": DESCR["causal_prefill"], "bound": "mfma",
+            "kernels": {"prefill_kernel": {"ms": st, "algorithmic_flops": flops,
+                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"])}},
+            "parity": parity_from_oracle(oc, "causal_prefill", w, r["out"], r["lse"]),
+            "cpu_baseline": oc.baselines.get("causal_prefill") if oc else None}
+
+
+def leg_decode(name, w, args, torch, dev, oc):
+    res = time_decode(w, args, torch, dev)
+    nbytes = decode_bytes(w)
+    dst, mst = stats_ms(res["decode"]), stats_ms(res["merge"])
+    kernels = {"decode_paged_kernel": {"ms": dst, "algorithmic_bytes": nbytes,
+                                       "roofline": roofline_entry("decode_paged_kernel", "hbm", nbytes, dst["mean"])}}
+    if res["splits"] > 1:
+        part = 2 * w.batch * w.num_qo_heads * res["splits"] * (w.head_dim + 1) * 4
+        kernels["merge_kernel"] = {"ms": mst, "partials_bytes": part}
+    entry = {"workload": DESCR[name], "bound": "hbm", "num_splits": res["splits"],
+             "step_ms_graph": round(res["step_ms"], 5), "step_ms_eager": round(res["step_ms_eager"], 5),
+             "step_GBs": round(nbytes / (res["step_ms"] * 1e-3) / 1e9, 1),
+             "kernels": kernels,
+             "parity": parity_from_oracle(oc, name, w, res["out"], res["lse"]),
+             "cpu_baseline": oc.baselines.get(name) if oc else None}
+    return entry, res
+
+
+def leg_mixed(w, window, args, torch, dev, oc):
+    """The mixed batch under one window: the whole call (prefill kernel, then
+    the decode kernel for the single-row requests), and each part alone as
+    its own call over the same pool (the prefill requests through
+    sinkattn_prefill, the decode rows through sinkattn_decode_paged)."""
+    import ctypes
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import binding
+    name = "mixed_batch_w128" if window else "mixed_batch_full"
+    n_pre = int(w.meta["n_prefill"])
+    d = Dev(w, torch, dev)
+    n = 30 if window == 0 else 100
+    whole = time_prefill(w, n, 3, torch, dev, window=window, d=d)
+    pre_w = sub_batch(w, range(n_pre))
+    dp = Dev.__new__(Dev)
+    dp.__dict__ = dict(d.__dict__)
+    dp.q = d.q[:int(w.qo_indptr[n_pre])]
+    dp.qo_indptr = d.qo_indptr[:n_pre + 1]
+    dp.kv_indptr = d.kv_indptr[:n_pre + 1]
+    dp.kv_len = d.kv_len[:n_pre]
+    pre = time_prefill(pre_w, n, 3, torch, dev, window=window, d=dp)
+    # decode rows: request b >= n_pre owns row qo_indptr[b] = d0 + (b - n_pre)
+    d0 = int(w.qo_indptr[n_pre])
+    dec_w = sub_batch(w, range(n_pre, w.batch))
+    q_dec = d.q[d0:]
+    out_dec = torch.empty_like(q_dec)
+    kv = binding.kv_descriptor(d.k, d.v, d.kv_indptr[n_pre:], d.page_indices, d.kv_len[n_pre:])
+    lib = sa.load_library()
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = ctypes.c_void_p
+    nd = w.batch - n_pre
+
+    def dec_call(i=0):
+        st = lib.sinkattn_decode_paged(P(q_dec.data_ptr()), ctypes.byref(kv), P(d.sinks.data_ptr()), 1,
+                                       P(out_dec.data_ptr()), None, None, None, nd, w.num_qo_heads,
+                                       w.num_kv_heads, 64, ctypes.c_float(w.scale), window, sp)
         if st != 0:
             raise RuntimeError(lib.sinkattn_last_error().decode())
-    e1.record(stream)
-    if s > 1:
-        for i in range(args.steps):
-            lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[i % len(reps)], lsep, sp)
-    e2.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / args.steps
-    mer_ms = e1.elapsed_time(e2) / args.steps if s > 1 else 0.0
-    return dict(step_ms=wall * 1e3, step_ms_eager=wall_eager * 1e3, decode_ms=dec_ms, merge_ms=mer_ms, splits=s,
-                out=out_host)
 
+    for _ in range(3):
+        dec_call()
+    dec_t = launch_times(dec_call, n, stream, torch)
+    torch.cuda.synchronize()
+    same = bool(np.array_equal(to_host(out_dec), whole["out"][d0:]))
+    flops = prefill_flops(pre_w, window)
+    nbytes = decode_bytes(dec_w, window)
+    wst, pst, dst = stats_ms(whole["times"]), stats_ms(pre["times"]), stats_ms(dec_t)
+    bound_ms = flops / (MFMA_PEAK_TFLOPS * 1e12) * 1e3 + nbytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    return {"workload": DESCR["mixed_batch"] + f"; window {window or 'none (full causal)'}",
+            "bound": "mfma (prefill part) + hbm (decode part)" if window == 0 else "latency",
+            "call_ms": wst,
+            "sum_of_roofline_ms": round(bound_ms, 5),
+            "call_frac_of_sum_bound": round(bound_ms / wst["mean"], 4),
+            "kernels": {
+                "prefill_kernel": {"ms": pst, "algorithmic_flops": flops, "rows": d0,
+                                   "roofline": roofline_entry("prefill_kernel", "mfma", flops, pst["mean"])},
+                "decode_paged_kernel": {"ms": dst, "algorithmic_bytes": nbytes, "rows": nd,
+                                        "roofline": roofline_entry("decode_paged_kernel", "hbm", nbytes,
+                                                                   dst["mean"])}},
+            "decode_rows_alone_equal_whole_call": same,
+            "parity": parity_from_oracle(oc, name, w, whole["out"], whole["lse"]),
+            "cpu_baseline": oc.baselines.get(name) if oc else None}
+
+
+# ---------------------------------------------------------------------------
+# main
+# ---------------------------------------------------------------------------
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); sharding the path over several "
+              "GPUs is not built", file=sys.stderr)
+        sys.exit(2)
+    if args.workload is not None:
+        return profile_only(args)
+    from gqa_attention_sinks_amd import workloads as wl
+    t_start = time.perf_counter()
+    log("generating workloads")
+    ws = {n: getattr(wl, n)() for n in ["tiny_prefill", "paged_decode", "causal_prefill", "long_split_decode",
+                                         "mixed_batch"]}
+    cores = len(os.sched_getaffinity(0))
+    oc = None
+    if not args.no_cpu:
+        log(f"oracle on {cores} host cores ({cpu_model()})")
+        oc = run_oracles(ws, cores)       # before the GPU is touched: the pool forks
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import gqa_attention_sinks_amd as sa
+    if not os.path.exists(sa.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    sa.load_library()
+    dev = torch.device("cuda:0")
+
+    configs = {}
+    log("paged_decode")
+    head, res = leg_decode("paged_decode", ws["paged_decode"], args, torch, dev, oc)
+    configs["paged_decode"] = head
+    torch.cuda.empty_cache()
+    log("tiny_prefill")
+    configs["tiny_prefill"] = leg_tiny(ws["tiny_prefill"], args, torch, dev, oc)
+    log("causal_prefill")
+    configs["causal_prefill"] = leg_causal_prefill(ws["causal_prefill"], args, torch, dev, oc)
+    torch.cuda.empty_cache()
+    log("long_split_decode")
+    configs["long_split_decode"], _ = leg_decode("long_split_decode", ws["long_split_decode"], args, torch,
+                                                 dev, oc)
+    torch.cuda.empty_cache()
+    for window in (128, 0):
+        log(f"mixed_batch window={window}")
+        configs["mixed_batch_w128" if window else "mixed_batch_full"] = leg_mixed(ws["mixed_batch"], window,
+                                                                                  args, torch, dev, oc)
+        torch.cuda.empty_cache()
+
+    w = ws["paged_decode"]
+    nbytes = decode_bytes(w)
+    value = nbytes / (res["step_ms"] * 1e-3) / 1e9
+    dmean = head["kernels"]["decode_paged_kernel"]["ms"]["mean"]
+    roof = roofline_entry("decode_paged_kernel", "hbm", nbytes, dmean,
+                          measured_traffic("decode_paged_kernel", "paged_decode", res["splits"]))
+    pre = configs["causal_prefill"]["kernels"]["prefill_kernel"]
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": DESCR["paged_decode"],
+            "num_splits": res["splits"],
+            "kv_replicas_rotated": args.replicas,
+            "algorithmic_bytes": nbytes,
+            "compute": "bf16 Q.K^T and fp16 P.V on MFMA, fp32 accumulation",
+            "step": "K steps (decode + merge launches) captured in one HIP graph, replayed",
+            "ms_per_step_eager": round(res["step_ms_eager"], 5),
+            "decode_kernel_ms": head["kernels"]["decode_paged_kernel"]["ms"],
+            "merge_kernel_ms": head["kernels"].get("merge_kernel", {}).get("ms"),
+            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
+        },
+        "roofline": roof,
+        "prefill": {
+            "workload": DESCR["causal_prefill"],
+            "value": pre["roofline"]["achieved"],
+            "unit": "TFLOP/s",
+            "ms_per_call": pre["ms"]["mean"],
+            "algorithmic_flops": pre["algorithmic_flops"],
+            "roofline": pre["roofline"],
+        },
+        "configs": configs,
+    }
+    if oc is not None:
+        cb = dict(oc.baselines["paged_decode"])
+        cb.pop("seconds", None)
+        cb["cpu_model"] = cpu_model()
+        cb["configs"] = {k: v for k, v in oc.baselines.items()}
+        line["cpu_baseline"] = cb
+        line["parity"] = head["parity"]
+        line["parity_all_within_tol"] = all(c["parity"]["within_tol"] for c in configs.values() if c.get("parity"))
+    line["bench_seconds"] = round(time.perf_counter() - t_start, 1)
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# one workload only (for rocprofv3 runs)
+# ---------------------------------------------------------------------------
 
 def time_verify(w, args, torch, dev):
     """Several query rows per request (sinkattn_decode_paged_multi): the
-    decode kernel alone between two events on its stream, replicas rotated,
-    and the whole step (decode + merge) by wall clock."""
+    decode kernel alone per launch, replicas rotated, and the whole step
+    (decode + merge) by wall clock."""
     import ctypes
     import gqa_attention_sinks_amd as sa
     from gqa_attention_sinks_amd import binding
@@ -258,42 +828,8 @@ def time_verify(w, args, torch, dev):
         call(i, True)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        call(i, False)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return dict(step_ms=wall * 1e3, decode_ms=e0.elapsed_time(e1) / args.steps, splits=s)
-
-
-def per_call_ms(call, args, torch):
-    """Time per call of a short kernel.  ``ms``: ``args.steps`` calls captured
-    in one HIP graph and replayed, so the host's launch rate does not enter
-    (these kernels run for a few microseconds, about what a launch from Python
-    costs); ``ms_eager``: the same calls issued one by one from Python."""
-    for _ in range(args.warmup):
-        call()
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(args.steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_eager = e0.elapsed_time(e1) / args.steps
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for _ in range(args.steps):
-            call()
-    g.replay()
-    torch.cuda.synchronize()
-    e0.record(stream)
-    g.replay()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / args.steps, ms_eager
+    dec = launch_times(lambda i: call(i, False), args.steps, stream, torch)
+    return dict(step_ms=wall * 1e3, decode=stats_ms(dec), splits=s)
 
 
 def time_append(args, torch, dev):
@@ -321,9 +857,12 @@ def time_append(args, torch, dev):
     table = torch.from_numpy(np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)).to(dev)
     q_out = torch.empty_like(q)
     args_ = (k, v, i32(append_indptr), kp, vp, i32(page_indptr), i32(page_indices), i32(kv_len), table)
-    ms, ms_eager = per_call_ms(lambda: sa.append_paged_kv_rope(*args_, q=q, q_out=q_out), args, torch)
+    call = lambda: sa.append_paged_kv_rope(*args_, q=q, q_out=q_out)
+    for _ in range(args.warmup):
+        call()
+    ms = graph_call_ms(call, args.steps, torch)
     nbytes = t * (2 * hq * 128 + 4 * hkv * 128 + 256) + 4 * (len(page_indices) + 3 * 17)
-    return dict(tokens=t, ms=ms, ms_eager=ms_eager, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
+    return dict(tokens=t, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
 
 
 def time_moe(args, torch, dev):
@@ -336,175 +875,26 @@ def time_moe(args, torch, dev):
     logits = logits.view(torch.bfloat16)
     idx = torch.empty((t, k), dtype=torch.int32, device=dev)
     w = torch.empty((t, k), dtype=torch.bfloat16, device=dev)
-    ms, ms_eager = per_call_ms(lambda: sa.moe_topk_softmax(logits, k, idx, w), args, torch)
+    call = lambda: sa.moe_topk_softmax(logits, k, idx, w)
+    for _ in range(args.warmup):
+        call()
+    ms = graph_call_ms(call, args.steps, torch)
     nbytes = t * (e * 2 + k * 6)
-    return dict(tokens=t, experts=e, top_k=k, ms=ms, ms_eager=ms_eager, bytes=nbytes,
-                GBs=nbytes / (ms * 1e-3) / 1e9)
+    return dict(tokens=t, experts=e, top_k=k, ms=ms, bytes=nbytes, GBs=nbytes / (ms * 1e-3) / 1e9)
 
 
-def time_prefill(w, steps, warmup, torch, dev, window=0):
-    from gqa_attention_sinks_amd import binding
-    d = Dev(w, torch, dev)
-    out = torch.empty_like(d.q)
-    stream = torch.cuda.current_stream()
-
-    host = np.ascontiguousarray(w.qo_indptr, dtype=np.int32)
-
-    def call():
-        binding.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale, window=window,
-                        page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out,
-                        qo_indptr_host=host)
-
-    for _ in range(warmup):
-        call()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(steps):
-        call()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = (time.perf_counter() - t0) / steps
-    return dict(step_ms=wall * 1e3, kernel_ms=e0.elapsed_time(e1) / steps, out=out)
-
-
-def measured_traffic(kernel, workload, splits):
-    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE runs, or
-    None when the kernel's sources changed since they were taken."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path)).get(kernel)
-    csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in ("decode.hip", "device_common.hpp", "kernel_args.hpp")]
-    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
-    if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
-            or rec.get("num_splits") != splits:
-        return None
-    return int(round(rec["bytes"]))
-
-
-def parity(g, r):
-    err = np.abs(g - r)
-    return dict(max_abs=float(err.max()), within_tol=bool(np.all(err <= 2e-3 + 1e-2 * np.abs(r))))
-
-
-def cpu_baseline(w, gpu_out, min_seconds=10.0):
-    """The fp64 oracle (as it stands) on the whole decode workload, one
-    thread, repeated until about ten seconds of CPU work have been timed (a
-    pass takes a fraction of a second); the rate is the mean over the
-    passes."""
-    import oracle
-    from threadpoolctl import threadpool_limits
-    kv = oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr, paged=True, page_indices=w.page_indices,
-                        kv_len=w.kv_len)
-    passes, dt = 0, 0.0
-    with threadpool_limits(limits=1):
-        while dt < min_seconds and passes < 1000:
-            t0 = time.perf_counter()
-            ro, _ = oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, 0, workers=1)
-            dt += time.perf_counter() - t0
-            passes += 1
-    return dict(value=passes * decode_bytes(w) / dt / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys), fp64 numpy, "
-                       f"{passes} passes in {dt:.1f} s", seconds=dt), parity(gpu_out, ro)
-
-
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); sharding the path over several "
-              "GPUs is not built", file=sys.stderr)
-        sys.exit(2)
+def profile_only(args):
+    """Time one named workload only (for rocprofv3 runs)."""
     import torch
+    import gqa_attention_sinks_amd as sa
+    from gqa_attention_sinks_amd import workloads as wl
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
-    import gqa_attention_sinks_amd as sa
-    from gqa_attention_sinks_amd import workloads as wl
-    if not os.path.exists(sa.library_path()):
-        import __graft_entry__
-        __graft_entry__.build()
     sa.load_library()
     dev = torch.device("cuda:0")
-
-    if args.workload not in ("paged_decode",):
-        return profile_only(args, torch, dev, wl)
-
-    log("generating paged_decode workload")
-    w = wl.paged_decode()
-    res = time_decode(w, args, torch, dev)
-    nbytes = decode_bytes(w)
-    value = nbytes / (res["step_ms"] * 1e-3) / 1e9
-    achieved = nbytes / (res["decode_ms"] * 1e-3) / 1e9
-    line = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(res["step_ms"], 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "paged decode: batch 64, one query token each, KV lengths uniform in [1, 4096], "
-                        "64 query / 8 KV heads, head_dim 64, page size 16, pages permuted in a shared pool, "
-                        "sinks N(0, 2), seed 0",
-            "num_splits": res["splits"],
-            "kv_replicas_rotated": args.replicas,
-            "algorithmic_bytes": nbytes,
-            "compute": "bf16 Q.K^T and fp16 P.V on MFMA, fp32 accumulation",
-            "step": "K steps (decode + merge launches) captured in one HIP graph, replayed",
-            "ms_per_step_eager": round(res["step_ms_eager"], 5),
-            "decode_kernel_ms": round(res["decode_ms"], 5),
-            "merge_kernel_ms": round(res["merge_ms"], 5),
-            "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
-        },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic("decode_paged_kernel", "paged_decode", res["splits"]),
-            "kernel": "decode_paged_kernel",
-        },
-    }
-    if not args.no_prefill:
-        log("generating causal_prefill workload")
-        wp = wl.causal_prefill()
-        pr = time_prefill(wp, args.prefill_steps, 3, torch, dev)
-        flops = prefill_flops(wp)
-        tflops = flops / (pr["kernel_ms"] * 1e-3) / 1e12
-        line["prefill"] = {
-            "workload": "causal prefill: batch 4 x 8192 tokens, 64 query / 8 KV heads, head_dim 64, contiguous KV, "
-                        "sinks N(0, 2)",
-            "value": round(tflops, 1),
-            "unit": "TFLOP/s",
-            "ms_per_call": round(pr["kernel_ms"], 4),
-            "algorithmic_flops": flops,
-            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                         "kernel": "prefill_kernel"},
-        }
-        del pr
-    if not args.no_cpu:
-        log("timing the oracle on the host")
-        cb, par = cpu_baseline(w, res["out"])
-        line["cpu_baseline"] = {k: v for k, v in cb.items() if k != "seconds"}
-        line["parity"] = par
-    print(json.dumps(line), flush=True)
-
-
-def profile_only(args, torch, dev, wl):
-    """Time one named workload only (for rocprofv3 runs)."""
-    if args.workload == "copy_calibration":
+    name = args.workload
+    if name == "copy_calibration":
         n = 256 << 20
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -514,38 +904,38 @@ def profile_only(args, torch, dev, wl):
             dst.copy_(src)
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / args.steps
-        print(json.dumps({"workload": "copy_calibration", "bytes_read": n, "bytes_written": n,
-                          "ms": dt * 1e3, "GBs_rw": 2 * n / dt / 1e9}))
+        print(json.dumps({"workload": name, "bytes_read": n, "bytes_written": n, "ms": dt * 1e3,
+                          "GBs_rw": 2 * n / dt / 1e9}))
         return
-    if args.workload == "moe_topk":
+    if name == "moe_topk":
         r = time_moe(args, torch, dev)
-        print(json.dumps({"workload": "moe_topk", **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
+        print(json.dumps({"workload": name, **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
         return
-    if args.workload == "append_rope":
+    if name == "append_rope":
         r = time_append(args, torch, dev)
-        print(json.dumps({"workload": "append_rope", **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
+        print(json.dumps({"workload": name, **r, "frac": r["GBs"] / HBM_PEAK_GBS}))
         return
-    w = getattr(wl, args.workload)()
-    log(f"timing {args.workload}")
-    if args.workload in ("verify_decode", "verify_tree"):
+    w = getattr(wl, name)()
+    log(f"timing {name}")
+    if name in ("verify_decode", "verify_tree"):
         res = time_verify(w, args, torch, dev)
-        gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9
-        print(json.dumps({"workload": args.workload, "rows": int(w.qo_indptr[-1]), "splits": res["splits"],
-                          "step_ms": res["step_ms"], "decode_ms": res["decode_ms"], "decode_GBs": gbs,
+        gbs = decode_bytes(w) / (res["decode"]["mean"] * 1e-3) / 1e9
+        print(json.dumps({"workload": name, "rows": int(w.qo_indptr[-1]), "splits": res["splits"],
+                          "step_ms": res["step_ms"], "decode_ms": res["decode"], "decode_GBs": gbs,
                           "frac": gbs / HBM_PEAK_GBS}))
         return
-    if args.workload == "long_split_decode":
-        res = time_decode(w, args, torch, dev)
-        gbs = decode_bytes(w) / (res["decode_ms"] * 1e-3) / 1e9
-        print(json.dumps({"workload": args.workload, "step_ms": res["step_ms"],
-                          "step_ms_eager": res["step_ms_eager"], "decode_ms": res["decode_ms"],
-                          "merge_ms": res["merge_ms"], "decode_GBs": gbs, "frac": gbs / HBM_PEAK_GBS}))
+    if name in ("paged_decode", "long_split_decode"):
+        entry, _ = leg_decode(name, w, args, torch, dev, None)
+        print(json.dumps({"workload": name, **entry}))
         return
-    for window in w.windows:
-        pr = time_prefill(w, args.steps, args.warmup, torch, dev, window=window)
-        flops = prefill_flops(w, window)
-        print(json.dumps({"workload": args.workload, "window": window, "ms": pr["kernel_ms"],
-                          "TFLOPs": flops / (pr["kernel_ms"] * 1e-3) / 1e12}))
+    if name == "tiny_prefill":
+        print(json.dumps({"workload": name, **leg_tiny(w, args, torch, dev, None)}))
+        return
+    if name == "causal_prefill":
+        print(json.dumps({"workload": name, **leg_causal_prefill(w, args, torch, dev, None)}))
+        return
+    for window in w.windows:                   # mixed_batch
+        print(json.dumps({"workload": name, "window": window, **leg_mixed(w, window, args, torch, dev, None)}))
 
 
 if __name__ == "__main__":

@@ -26,6 +26,7 @@ KV heads, head_dim 64, page size 16, softmax scale 1/sqrt(64).
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional, Sequence, Tuple
 
@@ -48,14 +49,33 @@ def bf16_bits(x) -> np.ndarray:
     return r
 
 
-def _normal_bf16(rng, shape, chunk=1 << 24) -> np.ndarray:
-    """Sequential fp32 standard-normal draws, rounded to bf16, without holding
-    the whole fp32 array (same stream as one large draw)."""
+def _normal_bf16(rng, shape, chunk=1 << 22) -> np.ndarray:
+    """fp32 standard-normal draws rounded to bf16, in chunks of ``chunk``
+    values.  Chunk i draws from its own PCG64 stream, seeded with
+    (key_i, i) where the keys are one draw of ``rng`` (so the result depends
+    only on ``rng``'s state, not on the thread count); the chunks are filled
+    by a thread pool, which keeps the multi-GB paged pools quick to build."""
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.uint16)
-    for s in range(0, n, chunk):
+    nchunks = max(1, -(-n // chunk))
+    keys = rng.integers(0, 1 << 62, size=nchunks)
+
+    def fill(i):
+        s = i * chunk
         e = min(n, s + chunk)
-        out[s:e] = bf16_bits(rng.standard_normal(e - s, dtype=np.float32))
+        sub = np.random.default_rng([int(keys[i]), i])
+        out[s:e] = bf16_bits(sub.standard_normal(e - s, dtype=np.float32))
+
+    if nchunks == 1:
+        fill(0)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        try:
+            cores = len(os.sched_getaffinity(0))
+        except AttributeError:          # pragma: no cover
+            cores = os.cpu_count() or 1
+        with ThreadPoolExecutor(max_workers=max(1, min(16, cores, nchunks))) as ex:
+            list(ex.map(fill, range(nchunks)))
     return out.reshape(shape)
 
 

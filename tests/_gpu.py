@@ -100,33 +100,22 @@ def kv_cache(w):
     return oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr)
 
 
-def oracle_full(w, window, sinks=True, workers=8):
+def host_workers():
+    """Oracle worker threads: every core this process may run on."""
+    return oracle.sink_attention.default_workers()
+
+
+def oracle_full(w, window, sinks=True, workers=None):
     return oracle.sink_attention_ref(w.q, w.qo_indptr, kv_cache(w), w.sinks if sinks else None,
-                                     w.scale, window, workers=workers)
+                                     w.scale, window, workers=workers or host_workers())
 
 
-def oracle_rows(w, rows, window, sinks=True):
-    """Oracle output for selected global query rows only.  Row t of a request
-    with n_q rows over n_k keys sees keys up to n_k - n_q + t, so it equals a
-    one-row request over the first n_k - n_q + t + 1 keys."""
-    out = np.zeros((len(rows), w.num_qo_heads, w.head_dim))
-    lse = np.zeros((len(rows), w.num_qo_heads))
-    req = np.searchsorted(w.qo_indptr, rows, side="right") - 1
-    for i, (r, b) in enumerate(zip(rows, req)):
-        n_q = int(w.qo_indptr[b + 1] - w.qo_indptr[b])
-        t = int(r - w.qo_indptr[b])
-        n_k = int(w.kv_len[b])
-        keep = n_k - n_q + t + 1
-        if w.paged:
-            kv = oracle.KVCache(k=w.k, v=w.v, kv_indptr=np.array([w.kv_indptr[b], w.kv_indptr[b + 1]]),
-                                paged=True, page_indices=w.page_indices, kv_len=np.array([keep]),
-                                page_size=w.page_size)
-        else:
-            base = int(w.kv_indptr[b])
-            kv = oracle.KVCache(k=w.k[base:base + keep], v=w.v[base:base + keep], kv_indptr=np.array([0, keep]))
-        o, l = oracle.sink_attention_ref(w.q[r:r + 1], [0, 1], kv, w.sinks if sinks else None, w.scale, window)
-        out[i], lse[i] = o[0], l[0]
-    return out, lse
+def assert_parity_by_request(w, g, r, what, lse_g, lse_r, requests=None):
+    """assert_parity on each request's rows in turn (bounds the temporaries of
+    full-size comparisons)."""
+    for b in (range(w.batch) if requests is None else requests):
+        lo, hi = int(w.qo_indptr[b]), int(w.qo_indptr[b + 1])
+        assert_parity(g[lo:hi], r[lo:hi], f"{what} request {b}", lse_g[lo:hi], lse_r[lo:hi])
 
 
 def assert_parity(g, r, what, lse_g=None, lse_r=None):

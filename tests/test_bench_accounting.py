@@ -19,10 +19,15 @@ import bench
 from gqa_attention_sinks_amd import workloads as wl
 
 
-def _decode_bytes_brute(w):
+def _decode_bytes_brute(w, window=0):
     total = 0
     for b in range(w.batch):
-        for _key in range(int(w.kv_len[b])):
+        n_q, n_k = int(w.qo_len[b]), int(w.kv_len[b])
+        for key in range(n_k):
+            # the key counts when some query row of the request sees it
+            seen = any(key <= n_k - n_q + t and (window == 0 or key > n_k - n_q + t - window) for t in range(n_q))
+            if not seen:
+                continue
             for _g in range(w.num_kv_heads):
                 total += 2 * w.head_dim * 2          # one K row and one V row, bf16
     rows = int(w.qo_indptr[-1])
@@ -55,6 +60,12 @@ def test_decode_bytes_several_rows():
     assert bench.decode_bytes(w) == _decode_bytes_brute(w)
 
 
+def test_decode_bytes_under_a_window():
+    w = wl.verify_decode(seed=3, batch=5, max_len=300, num_qo_heads=16, num_kv_heads=2)
+    for window in (1, 7, 128, 1000):
+        assert bench.decode_bytes(w, window) == _decode_bytes_brute(w, window), window
+
+
 def test_headline_decode_bytes():
     """The figure the profiles and the benchmark line quote."""
     assert bench.decode_bytes(wl.paged_decode()) == 274_846_980
@@ -76,3 +87,41 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert p.returncode == 2
     assert "one GPU" in p.stderr
+
+
+def test_oracle_legs_cover_the_rows_they_claim():
+    """The benchmark's oracle samples (sub-batches, (request, KV head)
+    units, split partials) reproduce the oracle's whole-call results on the
+    rows they cover: the parity summaries compare like with like."""
+    import oracle
+    ws = {
+        "tiny_prefill": wl.tiny_prefill(),
+        "paged_decode": wl.paged_decode(batch=6, max_len=200),
+        "causal_prefill": wl.causal_prefill(batch=2, seq=96, num_qo_heads=8, num_kv_heads=2),
+        "long_split_decode": wl.long_split_decode(batch=2, kv_len=700, num_splits=4, num_qo_heads=16,
+                                                  num_kv_heads=2),
+        "mixed_batch": wl.mixed_batch(n_prefill=3, chunk=40, max_prefix=100, n_decode=5, max_decode_len=300,
+                                      num_qo_heads=8, num_kv_heads=2),
+    }
+    oc = bench.run_oracles(ws, 3)
+    assert set(oc.baselines) == {"tiny_prefill", "paged_decode", "causal_prefill", "long_split_decode",
+                                 "mixed_batch_w128", "mixed_batch_full"}
+    for name, b in oc.baselines.items():
+        assert b["kind"] == "oracle" and b["value"] > 0 and 1 <= b["cores"] <= 3, name
+
+    def whole(w, window):
+        kv = (oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr, paged=True, page_indices=w.page_indices,
+                             kv_len=w.kv_len) if w.paged else oracle.KVCache(k=w.k, v=w.v, kv_indptr=w.kv_indptr))
+        return oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, window)
+
+    for name, key, window in [("tiny_prefill", "tiny_prefill", 0), ("paged_decode", "paged_decode", 0),
+                              ("causal_prefill", "causal_prefill", 0), ("long_split_decode", "long_split_decode", 0),
+                              ("mixed_batch_w128", "mixed_batch", 128), ("mixed_batch_full", "mixed_batch", 0)]:
+        w = ws[key]
+        out, lse = whole(w, window)
+        # the oracle's own results pass through the parity summary exactly
+        p = bench.parity_from_oracle(oc, name, w, out.astype(np.float32), lse.astype(np.float32))
+        assert p["within_tol"] and p["max_abs"] == 0.0 and p["lse_max_abs"] == 0.0, (name, p)
+        assert p["rows"] > 0
+    # the causal-prefill sample is the first three (request, KV head) units
+    assert [k for k, _, _ in oc.results["causal_prefill"]] == [(0, 0), (0, 1), (1, 0)]

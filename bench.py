@@ -262,17 +262,15 @@ def run_oracles(ws, cores):
     oc.run("paged_decode", jobs, decode_bytes(w), "GB/s",
            f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys) in {len(groups)} sub-batches",
            min_seconds=5.0)
-    # causal prefill: (request, KV head) units, one per core (at most all 32)
+    # causal prefill: every (request, KV head) unit
     w = ws["causal_prefill"]
-    units = [(u // w.num_kv_heads, u % w.num_kv_heads) for u in range(min(cores, w.batch * w.num_kv_heads))]
+    units = [(u // w.num_kv_heads, u % w.num_kv_heads) for u in range(w.batch * w.num_kv_heads)]
     jobs = []
     for b, g in units:
         jobs.append((kv_head_group(sub_batch(w, [b]), g), 0, "attn", (b, g)))
     flops = sum(prefill_flops(j[0]) for j in jobs)
     oc.run("causal_prefill", jobs, flops, "TFLOP/s",
-           f"{len(units)} of {w.batch * w.num_kv_heads} (request, KV head) units, every row of each "
-           f"({len(units) * (w.num_qo_heads // w.num_kv_heads)} of {w.batch * w.num_qo_heads} (request, head) "
-           f"pairs)")
+           f"whole workload as its {len(units)} (request, KV head) units")
     # long split decode: each request's 16 chunk partials and their merge
     w = ws["long_split_decode"]
     jobs = [(sub_batch(w, [b]), 0, "split", np.asarray([b])) for b in range(w.batch)]
@@ -287,15 +285,17 @@ def run_oracles(ws, cores):
     jobs = [(sub_batch(w, g), 128, "attn", np.asarray(g)) for g in groups]
     oc.run("mixed_batch_w128", jobs, prefill_flops(w, 128), "TFLOP/s",
            f"whole call ({w.batch} requests) in {len(groups)} sub-batches")
-    # mixed batch, full causal: every other prefill chunk, and every decode row
-    pre = list(range(0, n_pre, 2))
+    # mixed batch, full causal: every prefill chunk on its own, the decode rows
+    # in balanced sub-batches
+    pre = list(range(n_pre))
     dec = list(range(n_pre, w.batch))
     dec_groups = balanced_groups(np.asarray(w.kv_len)[dec], max(1, cores - len(pre)))
     jobs = [(sub_batch(w, [b]), 0, "attn", np.asarray([b])) for b in pre]
     jobs += [(sub_batch(w, [dec[i] for i in g]), 0, "attn", np.asarray([dec[i] for i in g])) for g in dec_groups]
     sample_w = sub_batch(w, pre + dec)
     oc.run("mixed_batch_full", jobs, prefill_flops(sample_w), "TFLOP/s",
-           f"{len(pre)} of {n_pre} prefill chunks (every other one) and all {len(dec)} decode rows")
+           f"whole call: the {len(pre)} prefill chunks one per job, the {len(dec)} decode rows in "
+           f"{len(dec_groups)} sub-batches")
     return oc
 
 
@@ -371,16 +371,25 @@ class Dev:
         return r
 
 
-def launch_times(fn, n, stream, torch):
-    """n calls of fn, each between two HIP events on ``stream`` (the events
-    are recorded back to back, so call i's time is e[i+1] - e[i])."""
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-    ev[0].record(stream)
-    for i in range(n):
-        fn(i)
-        ev[i + 1].record(stream)
+def launch_times(fn, n, stream, torch, group=10):
+    """Per-launch times of n calls of fn issued back to back on ``stream``:
+    the calls run in groups of ``group`` between two HIP events, and each
+    group gives one sample (its time / group).  Events between single
+    launches would add their own few microseconds to every sample; within a
+    group the launches follow each other as in a serving loop, so the mean
+    matches the kernel durations a profiler records (plus the short gaps
+    between launches)."""
+    groups = max(1, n // group)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * groups)]
+    i = 0
+    for gi in range(groups):
+        ev[2 * gi].record(stream)
+        for _ in range(group):
+            fn(i)
+            i += 1
+        ev[2 * gi + 1].record(stream)
     torch.cuda.synchronize()
-    return [ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+    return [ev[2 * gi].elapsed_time(ev[2 * gi + 1]) / group for gi in range(groups)]
 
 
 def to_host(t):
@@ -469,7 +478,7 @@ def time_decode(w, args, torch, dev, window=0):
     last = (args.steps - 1) % len(reps)
     out_host, lse_host = to_host(outs[last]), to_host(lses[last])
     del graph
-    n = max(args.steps, 100)
+    n = max(args.steps, 200)
     dec = launch_times(decode_only, n, stream, torch)
     mer = launch_times(merge_only, n, stream, torch) if s > 1 else [0.0]
     torch.cuda.synchronize()
@@ -477,7 +486,7 @@ def time_decode(w, args, torch, dev, window=0):
                 out=out_host, lse=lse_host)
 
 
-def time_prefill(w, n, warmup, torch, dev, window=0, d=None):
+def time_prefill(w, n, warmup, torch, dev, window=0, d=None, group=10):
     """sinkattn_prefill on a workload, each call between events; returns the
     per-call times and the output."""
     from gqa_attention_sinks_amd import binding
@@ -495,7 +504,7 @@ def time_prefill(w, n, warmup, torch, dev, window=0, d=None):
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
-    times = launch_times(call, n, stream, torch)
+    times = launch_times(call, n, stream, torch, group=group)
     return dict(times=times, out=to_host(out), lse=to_host(lse))
 
 
@@ -557,7 +566,7 @@ DESCR = {
 def leg_tiny(w, args, torch, dev, oc):
     import gqa_attention_sinks_amd as sa
     d = Dev(w, torch, dev)
-    r = time_prefill(w, max(args.steps, 100), args.warmup, torch, dev, d=d)
+    r = time_prefill(w, max(args.steps, 200), args.warmup, torch, dev, d=d)
     out = torch.empty_like(d.q)
     host = np.ascontiguousarray(w.qo_indptr, dtype=np.int32)
     graph_ms = graph_call_ms(lambda: sa.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale,
@@ -573,7 +582,7 @@ def leg_tiny(w, args, torch, dev, oc):
 
 
 def leg_causal_prefill(w, args, torch, dev, oc):
-    r = time_prefill(w, 30, 3, torch, dev)
+    r = time_prefill(w, 40, 3, torch, dev, group=2)
     flops = prefill_flops(w)
     st = stats_ms(r["times"])
     return {"workload": DESCR["causal_prefill"], "bound": "mfma",
@@ -612,8 +621,8 @@ def leg_mixed(w, window, args, torch, dev, oc):
     name = "mixed_batch_w128" if window else "mixed_batch_full"
     n_pre = int(w.meta["n_prefill"])
     d = Dev(w, torch, dev)
-    n = 30 if window == 0 else 100
-    whole = time_prefill(w, n, 3, torch, dev, window=window, d=d)
+    n, group = (40, 2) if window == 0 else (200, 10)
+    whole = time_prefill(w, n, 3, torch, dev, window=window, d=d, group=group)
     pre_w = sub_batch(w, range(n_pre))
     dp = Dev.__new__(Dev)
     dp.__dict__ = dict(d.__dict__)
@@ -621,7 +630,7 @@ def leg_mixed(w, window, args, torch, dev, oc):
     dp.qo_indptr = d.qo_indptr[:n_pre + 1]
     dp.kv_indptr = d.kv_indptr[:n_pre + 1]
     dp.kv_len = d.kv_len[:n_pre]
-    pre = time_prefill(pre_w, n, 3, torch, dev, window=window, d=dp)
+    pre = time_prefill(pre_w, n, 3, torch, dev, window=window, d=dp, group=group)
     # decode rows: request b >= n_pre owns row qo_indptr[b] = d0 + (b - n_pre)
     d0 = int(w.qo_indptr[n_pre])
     dec_w = sub_batch(w, range(n_pre, w.batch))
@@ -643,7 +652,7 @@ def leg_mixed(w, window, args, torch, dev, oc):
 
     for _ in range(3):
         dec_call()
-    dec_t = launch_times(dec_call, n, stream, torch)
+    dec_t = launch_times(dec_call, n, stream, torch, group=group)
     torch.cuda.synchronize()
     same = bool(np.array_equal(to_host(out_dec), whole["out"][d0:]))
     flops = prefill_flops(pre_w, window)
@@ -828,7 +837,7 @@ def time_verify(w, args, torch, dev):
         call(i, True)
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    dec = launch_times(lambda i: call(i, False), args.steps, stream, torch)
+    dec = launch_times(lambda i: call(i, False), max(args.steps, 100), stream, torch)
     return dict(step_ms=wall * 1e3, decode=stats_ms(dec), splits=s)
 
 

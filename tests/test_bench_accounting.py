@@ -123,5 +123,5 @@ def test_oracle_legs_cover_the_rows_they_claim():
         p = bench.parity_from_oracle(oc, name, w, out.astype(np.float32), lse.astype(np.float32))
         assert p["within_tol"] and p["max_abs"] == 0.0 and p["lse_max_abs"] == 0.0, (name, p)
         assert p["rows"] > 0
-    # the causal-prefill sample is the first three (request, KV head) units
-    assert [k for k, _, _ in oc.results["causal_prefill"]] == [(0, 0), (0, 1), (1, 0)]
+    # the causal-prefill sample is every (request, KV head) unit
+    assert [k for k, _, _ in oc.results["causal_prefill"]] == [(0, 0), (0, 1), (1, 0), (1, 1)]

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     append_paged_kv_rope,
     decode_paged,
     decode_paged_multi,
+    decode_paged_noalloc,
     kv_descriptor,
     library_path,
     load_library,

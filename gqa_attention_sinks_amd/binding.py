@@ -23,9 +23,11 @@ MAX_SPLITS = 256
 MAX_DECODE_ROWS = 8
 MAX_EXPERTS = 512
 MAX_TOP_K = 8
+NOALLOC_SCRATCH_BYTES = 8 << 20
 EXPORTED = (
     "sinkattn_prefill",
     "sinkattn_decode_paged",
+    "sinkattn_decode_paged_noalloc",
     "sinkattn_decode_paged_multi",
     "sinkattn_append_paged_kv_rope",
     "sinkattn_moe_topk_softmax",
@@ -83,6 +85,9 @@ def load_library():
     lib.sinkattn_decode_paged.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp, vp, i32, i32,
                                           i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged.restype = i32
+    lib.sinkattn_decode_paged_noalloc.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, i32, i32, i32, i32,
+                                                  f32, i32, vp]
+    lib.sinkattn_decode_paged_noalloc.restype = i32
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp,
                                                 vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged_multi.restype = i32
@@ -271,6 +276,35 @@ def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm
                                      float(sm_scale), int(window), _stream(stream)))
     if not want_out:
         return o_part, lse_part
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_paged_noalloc(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm_scale: float,
+                         num_splits: int = 1, window: int = 0, out=None, lse=None, return_lse: bool = False,
+                         stream=None):
+    """``sinkattn_decode_paged_noalloc``: like :func:`decode_paged` with the
+    merge, the split partials in the library's own device array (nothing is
+    allocated by the library; ``out`` and ``lse`` are allocated here when not
+    given).  Returns ``out`` (and ``lse``)."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, Hq, 64]")
+    batch, hq, _ = q.shape
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32, (hq,))
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, q.shape)
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, hq))
+    lib = load_library()
+    _check(lib.sinkattn_decode_paged_noalloc(_ptr(q), ctypes.byref(kvs), _ptr(sinks), int(num_splits), _ptr(out),
+                                             _ptr(lse), batch, hq, k_pool.shape[1], HEAD_DIM, float(sm_scale),
+                                             int(window), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

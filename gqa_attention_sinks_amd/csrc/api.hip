@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "kernel_args.hpp"
@@ -66,6 +67,35 @@ sinkattn_status check_kv(const sinkattn_kv* kv, bool need_paged) {
     REQUIRE(kv->page_size == SINKATTN_PAGE_SIZE, SINKATTN_ERR_UNSUPPORTED,
             "page_size %d unsupported (only 16)", kv->page_size);
   }
+  return SINKATTN_OK;
+}
+
+// Partials of sinkattn_decode_paged_noalloc: a file-scope device array, one
+// copy per GPU at its own address.  Host code never passes `scratch` itself
+// to a kernel (in host code the name is only a stand-in for the symbol): it
+// uses the device address that hipGetSymbolAddress returns for the current
+// device, looked up on the first call there and kept per device.
+__device__ __align__(256) unsigned char scratch[SINKATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+sinkattn_status scratch_on_current_device(void** ptr) {
+  int dev = -1;
+  sinkattn_status st = hip_status(hipGetDevice(&dev), "hipGetDevice");
+  if (st != SINKATTN_OK) return st;
+  REQUIRE(dev >= 0 && dev < kMaxDevices, SINKATTN_ERR_UNSUPPORTED, "device %d: at most %d devices", dev,
+          kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    st = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (st != SINKATTN_OK) return st;
+    REQUIRE(p != nullptr, SINKATTN_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return SINKATTN_OK;
 }
 
@@ -200,6 +230,36 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
     if ((st = hip_status(sinkattn::launch_merge(m, s), "merge launch")) != SINKATTN_OK) return st;
   }
   return SINKATTN_OK;
+}
+
+sinkattn_status sinkattn_decode_paged_noalloc(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                              int32_t num_splits, void* out, float* lse, int32_t batch,
+                                              int32_t num_qo_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, float sm_scale, int32_t window,
+                                              void* stream) {
+  REQUIRE(q != nullptr && out != nullptr, SINKATTN_ERR_INVALID_ARG, "q and out are required");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
+  if (st != SINKATTN_OK) return st;
+  if ((st = check_kv(kv, true)) != SINKATTN_OK) return st;
+  REQUIRE(num_splits >= 1 && num_splits <= SINKATTN_MAX_SPLITS, SINKATTN_ERR_INVALID_ARG,
+          "num_splits must be in [1, %d] (got %d)", SINKATTN_MAX_SPLITS, num_splits);
+  if (num_splits == 1)   // nothing to merge: no partials, no scratch
+    return sinkattn_decode_paged(q, kv, sinks, 1, out, nullptr, nullptr, lse, batch, num_qo_heads, num_kv_heads,
+                                 head_dim, sm_scale, window, stream);
+  // o_part [batch, Hq, S, 64] then lse_part [batch, Hq, S], each 256-byte aligned
+  const size_t parts = (size_t)batch * num_qo_heads * num_splits;
+  const size_t o_bytes = (parts * SINKATTN_HEAD_DIM * sizeof(float) + 255) & ~(size_t)255;
+  const size_t need = o_bytes + parts * sizeof(float);
+  REQUIRE(need <= SINKATTN_NOALLOC_SCRATCH_BYTES, SINKATTN_ERR_INVALID_ARG,
+          "batch %d x %d heads x %d splits needs %zu bytes of partials, more than the %u-byte scratch "
+          "array; use sinkattn_decode_paged with caller-owned partials", batch, num_qo_heads, num_splits, need,
+          (unsigned)SINKATTN_NOALLOC_SCRATCH_BYTES);
+  void* base = nullptr;
+  if ((st = scratch_on_current_device(&base)) != SINKATTN_OK) return st;
+  float* o_part = static_cast<float*>(base);
+  float* lse_part = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + o_bytes);
+  return sinkattn_decode_paged(q, kv, sinks, num_splits, out, o_part, lse_part, lse, batch, num_qo_heads,
+                               num_kv_heads, head_dim, sm_scale, window, stream);
 }
 
 sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,

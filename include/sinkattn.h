@@ -78,6 +78,7 @@ extern "C" {
 #define SINKATTN_MAX_DECODE_ROWS 8
 #define SINKATTN_MAX_EXPERTS 512
 #define SINKATTN_MAX_TOP_K 8
+#define SINKATTN_NOALLOC_SCRATCH_BYTES (8u << 20) /* partials of sinkattn_decode_paged_noalloc */
 
 typedef enum {
   SINKATTN_OK = 0,
@@ -166,6 +167,28 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
                                       int32_t num_qo_heads, int32_t num_kv_heads,
                                       int32_t head_dim, float sm_scale, int32_t window,
                                       void* stream);
+
+/* sinkattn_decode_paged for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  Same computation, arguments and results as
+ * sinkattn_decode_paged with out given (the split partials are merged into
+ * out, and lse, if given, gets the final LSE), but the caller passes no
+ * partial buffers: for num_splits > 1 they live in a device array owned by
+ * the library, SINKATTN_NOALLOC_SCRATCH_BYTES (8 MiB) per GPU, held until
+ * the process ends.  Its address on the current device is looked up on the
+ * first call there (`stream` must belong to the current device).  The
+ * partials need batch * Hq * num_splits * 65 * 4 bytes (plus 256 of
+ * alignment); larger calls are rejected with SINKATTN_ERR_INVALID_ARG before
+ * anything is enqueued -- use sinkattn_decode_paged with caller-owned
+ * partials for them.  No call allocates or frees memory.  Every call on one
+ * GPU shares that array: calls that may overlap on a GPU (concurrent streams,
+ * several host threads) race and must be ordered by the caller; nothing in it
+ * needs clearing between calls (each call writes every partial it reads). */
+sinkattn_status sinkattn_decode_paged_noalloc(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                              int32_t num_splits, void* out, float* lse, int32_t batch,
+                                              int32_t num_qo_heads, int32_t num_kv_heads,
+                                              int32_t head_dim, float sm_scale, int32_t window,
+                                              void* stream);
 
 /* Several query rows per request over a paged KV cache, split along the KV
  * sequence like sinkattn_decode_paged: the step in which the target model

@@ -327,3 +327,18 @@ def test_last_hip_error_is_the_last_error(lib):
     assert _decode(lib, _kv(), s=0) == INVALID
     assert lib.sinkattn_last_hip_error() == lib.sinkattn_last_error()
     assert b"num_splits" in lib.sinkattn_last_hip_error()
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch(lib):
+    """The size check comes before any HIP call: 64 requests x 64 heads x 256
+    splits need 272 MB of partials, beyond the 8 MiB array."""
+    kv = _kv()
+    f = lib.sinkattn_decode_paged_noalloc
+    assert f(FAKE, ctypes.byref(kv), None, 256, FAKE, None, 64, 64, 8, 64, ctypes.c_float(0.125), 0, None) == INVALID
+    msg = lib.sinkattn_last_error()
+    assert b"scratch" in msg and b"caller-owned" in msg
+    assert f(None, ctypes.byref(kv), None, 2, FAKE, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0, None) == INVALID
+    assert f(FAKE, ctypes.byref(kv), None, 2, None, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0, None) == INVALID
+    assert f(FAKE, ctypes.byref(kv), None, 0, FAKE, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0, None) == INVALID
+    assert f(FAKE, ctypes.byref(_kv(paged=0)), None, 2, FAKE, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0,
+             None) == INVALID

@@ -45,6 +45,9 @@ from .sink_attention import (  # noqa: F401
     merge_ref,
     attention_weights_ref,
     visible_range,
+    live_pages_ref,
+    balanced_pieces_ref,
+    pieces_partials_ref,
 )
 from .rope_append import append_rope_ref, append_positions, rotate  # noqa: F401
 from .moe_routing import topk_softmax_ref  # noqa: F401

@@ -42,6 +42,15 @@ Readings of points the pages leave open (each enforced by a test):
 * R10 lse is the natural log of Z and includes the sink.
 * R14 no visible key: o = 0 and lse = sink; sink = +inf: o = 0, lse = +inf;
       sink = -inf and no visible key: o = 0, lse = -inf.
+* R24 balanced split of a decode batch (one query row per request, at
+      n_k - 1): the keys a row reads are [lo, n_k), lo = max(0, n_k - W)
+      under a window W > 0, else 0, i.e. its live pages floor(lo / 16) ..
+      ceil(n_k / 16) - 1.  The requests' live pages, request after request,
+      form one list of T pages; segment s of N holds the list positions
+      [floor(s T / N), floor((s + 1) T / N)).  A request's piece in a
+      segment is the part of its live pages there (its keys clipped to
+      [lo, n_k)); each request's first piece carries the sink.  A request
+      with no key has one empty piece (o = 0, lse = sink).
 * R18 custom masks (a draft tree verified in one step): when a boolean mask
       ``[n_q, n_k]`` is given for a request, key j is visible to row t
       exactly when ``mask[t, j]``; it replaces the causal rule and the window,
@@ -351,6 +360,84 @@ def split_partials_ref(q, kv: KVCache, sinks, scale: float, num_splits: int, win
 
     _run_units(unit, [(b, g) for b in range(batch) for g in range(hkv)], workers)
     return o_part, lse_part
+
+
+def live_pages_ref(kv_len, window: int = 0, page_size: int = 16):
+    """The pages one query row at position n_k - 1 reads (R24): keys
+    [lo, n_k) with lo = max(0, n_k - W) for a window W > 0, else 0, on pages
+    floor(lo / page_size) .. ceil(n_k / page_size) - 1.  Returns int64
+    arrays (first_page, n_pages, lo), one entry per request."""
+    n_k = np.asarray(kv_len, dtype=np.int64)
+    lo = np.maximum(0, n_k - window) if window > 0 else np.zeros_like(n_k)
+    first = lo // page_size
+    end = -(-n_k // page_size)
+    return first, np.maximum(0, end - first), lo
+
+
+def balanced_pieces_ref(kv_len, num_segments: int, window: int = 0, page_size: int = 16):
+    """The balanced split of a decode batch into ``num_segments`` segments
+    (R24; [DAY0-SINK]: attention split into blocks along the KV sequence).
+    Returns one list per request of pieces ``(segment, lo_token, hi_token)``
+    in key order; a request with no key gets ``[(-1, 0, 0)]``."""
+    n_k = np.asarray(kv_len, dtype=np.int64)
+    first, n_pages, lo = live_pages_ref(n_k, window, page_size)
+    total = int(n_pages.sum())
+    starts = [(s * total) // num_segments for s in range(num_segments + 1)]
+    pieces = []
+    pos = 0                                   # list position of the request's first live page
+    for b in range(len(n_k)):
+        mine = []
+        for s in range(num_segments):
+            a = max(pos, starts[s])
+            e = min(pos + int(n_pages[b]), starts[s + 1])
+            if a >= e:
+                continue
+            p0 = int(first[b]) + (a - pos)    # the request's own page numbers
+            p1 = int(first[b]) + (e - pos)
+            mine.append((s, max(p0 * page_size, int(lo[b])), min(p1 * page_size, int(n_k[b]))))
+        pieces.append(mine if mine else [(-1, 0, 0)])
+        pos += int(n_pages[b])
+    return pieces
+
+
+def pieces_partials_ref(q, kv: KVCache, sinks, scale: float, pieces, window: int = 0,
+                        sink_in_every_piece: bool = False):
+    """Partial results of a decode step split into arbitrary pieces of each
+    request's keys ([DAY0-SINK]: only the first block carries the sink).
+    ``q`` is ``[B, Hq, D]`` (one query row per request, at ``kv_len[b] - 1``);
+    ``pieces[b]`` lists ``(segment, lo, hi)`` token ranges in key order (as
+    ``balanced_pieces_ref`` returns).  Each piece is attended on its own,
+    over its keys inside the row's visible range (R7), its softmax seeded
+    with the sink only when it is the request's first piece.  Returns one
+    ``(o [Hq, n_pieces, D], lse [Hq, n_pieces])`` pair per request, each
+    piece normalised by its own denominator (``merge_ref`` combines them).
+
+    ``sink_in_every_piece`` exists only as the negative control for tests."""
+    qf = _as_f64(q)
+    batch, hq, d = qf.shape
+    hkv = kv.k.shape[1]
+    group = hq // hkv
+    sk = _sinks_f64(sinks, hq)
+    out = []
+    for b in range(batch):
+        n_k = kv.length(b)
+        lo_vis, p = visible_range(1, n_k, 0, window)
+        lo_vis, p = int(lo_vis), int(p)
+        o_b = np.zeros((hq, len(pieces[b]), d))
+        l_b = np.empty((hq, len(pieces[b])))
+        for i, (_seg, lo, hi) in enumerate(pieces[b]):
+            a, e = max(lo, lo_vis), min(hi, p + 1)
+            for g in range(hkv):
+                kk, vv = kv.rows(b, g, a, max(a, e))
+                for h in range(g * group, (g + 1) * group):
+                    seeded = i == 0 or sink_in_every_piece
+                    sink = np.array([sk[h] if seeded else _NEG_INF])
+                    s_row = scale * (kk @ qf[b, h, :])[None, :]
+                    o, l = _softmax_with_sink(s_row, np.ones_like(s_row, dtype=bool), sink, vv)
+                    o_b[h, i, :] = o[0]
+                    l_b[h, i] = l[0]
+        out.append((o_b, l_b))
+    return out
 
 
 def merge_ref(o_part, lse_part):

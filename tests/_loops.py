@@ -159,3 +159,62 @@ def brute_attention_masked(q, qo_indptr, kvspec, sinks, scale, masks, num_kv_hea
             out.append(o_row)
             lse.append(l_row)
     return out, lse
+
+
+def brute_balanced(q, kvspec, sinks, scale, window, num_kv_heads, num_segments):
+    """The balanced split of a decode batch, token by token: one query row per
+    request at position n_k - 1 sees keys max(0, n_k - W) .. n_k - 1 (all of
+    them without a window); the pages holding those keys, request after
+    request, are numbered 0 .. T - 1, and page number i belongs to the first
+    segment s with i < floor((s + 1) T / N).  Each request's keys are grouped
+    by segment, every group attended on its own, the first one with the sink.
+    Returns per request a list of (segment, first key, last key + 1,
+    o[h][d], lse[h]); a request with no key gets one empty group (segment
+    -1) holding o = 0 and lse = sink."""
+    ps = kvspec["page_size"]
+    n_heads = len(sinks)
+    group = n_heads // num_kv_heads
+    live = []                                       # per request: its visible keys
+    for b in range(len(kvspec["kv_len"])):
+        n_k = kvspec["kv_len"][b]
+        first = max(0, n_k - window) if window > 0 else 0
+        live.append(list(range(first, n_k)))
+    numbers, total = [], 0                          # per request: page -> list number
+    for keys in live:
+        pages = sorted(set(j // ps for j in keys))
+        numbers.append({p: total + i for i, p in enumerate(pages)})
+        total += len(pages)
+
+    def segment_of(i):
+        s = 0
+        while not i < ((s + 1) * total) // num_segments:
+            s += 1
+        return s
+
+    result = []
+    for b, keys in enumerate(live):
+        groups = {}
+        for j in keys:
+            groups.setdefault(segment_of(numbers[b][j // ps]), []).append(j)
+        entries = []
+        for n, s in enumerate(sorted(groups)):
+            js = groups[s]
+            o_h, l_h = [], []
+            for h in range(n_heads):
+                rows = _key_rows(kvspec, b, h // group)
+                weights = [math.exp(scale * math.fsum(x * y for x, y in zip(q[b][h], rows[j][0]))) for j in js]
+                sink_w = [math.exp(sinks[h])] if n == 0 else []
+                z = math.fsum(weights + sink_w)
+                d = len(q[b][h])
+                if z == 0.0:
+                    o_h.append([0.0] * d)
+                    l_h.append(-math.inf)
+                    continue
+                o_h.append([math.fsum(w * rows[j][1][i] for w, j in zip(weights, js)) / z for i in range(d)])
+                l_h.append(math.log(z))
+            entries.append((s, js[0], js[-1] + 1, o_h, l_h))
+        if not entries:
+            d = len(q[b][0])
+            entries.append((-1, 0, 0, [[0.0] * d for _ in range(n_heads)], [float(x) for x in sinks]))
+        result.append(entries)
+    return result

@@ -50,7 +50,7 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 MFMA, vendor spec
 METRIC = "decode HBM GB/s (% peak) + prefill TFLOP/s (% MFMA peak), oracle-matched"
 ATOL, RTOL = 2e-3, 1e-2        # per element |gpu - ref| <= ATOL + RTOL * |ref|
 
-WORKLOADS = ["paged_decode", "tiny_prefill", "causal_prefill", "long_split_decode", "mixed_batch",
+WORKLOADS = ["paged_decode", "tiny_prefill", "causal_prefill", "long_split_decode", "mixed_batch", "skewed_decode",
              "verify_decode", "verify_tree", "append_rope", "moe_topk", "copy_calibration"]
 
 
@@ -63,7 +63,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=100)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--splits", type=int, default=0, help="decode split count (0: library's pick)")
+    p.add_argument("--splits", type=int, default=0, help="split decode: split count (0: library's pick)")
+    p.add_argument("--segments", type=int, default=0, help="balanced decode: segment count (0: library's pick)")
+    p.add_argument("--decode", default="split", choices=["balanced", "split"],
+                   help="the decode path of the headline (the other is timed beside it)")
     p.add_argument("--replicas", type=int, default=3)
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (no cpu_baseline, no parity)")
     p.add_argument("--workload", default=None, choices=WORKLOADS,
@@ -277,6 +280,12 @@ def run_oracles(ws, cores):
     oc.run("long_split_decode", jobs, decode_bytes(w), "GB/s",
            f"whole workload ({w.batch} requests x {int(w.kv_len[0])} keys, {w.num_splits} chunk partials "
            f"+ merge), one request per process")
+    # skewed decode: the long request alone, the rest in balanced sub-batches
+    w = ws["skewed_decode"]
+    groups = [[0]] + [[b + 1 for b in g] for g in balanced_groups(w.kv_len[1:], max(1, cores - 1))]
+    jobs = [(sub_batch(w, g), 0, "attn", np.asarray(g)) for g in groups]
+    oc.run("skewed_decode", jobs, decode_bytes(w), "GB/s",
+           f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys) in {len(groups)} sub-batches")
     # mixed batch, 128-key window: the whole call
     w = ws["mixed_batch"]
     n_pre = int(w.meta["n_prefill"])
@@ -396,24 +405,25 @@ def to_host(t):
     return t.float().cpu().numpy()
 
 
-def time_decode(w, args, torch, dev, window=0):
-    """Split decode + merge steps through the C ABI with prebuilt arguments
-    (the Python binding's checks would otherwise cost more than a step).  The
-    step time is that of the K steps captured in one HIP graph and replayed
-    (as a serving loop issues its decode steps); the same steps issued one by
-    one from Python are timed beside it; then each kernel is timed per launch
-    with events.  The output returned is the graph replay's."""
+def time_decode(w, args, torch, dev, window=0, mode="balanced"):
+    """Decode steps through the C ABI with prebuilt arguments (the Python
+    binding's checks would otherwise cost more than a step).  ``mode``:
+    "balanced" (sinkattn_decode_paged_balanced: the batch's live pages in
+    equal segments, then the merge of the requests that cross segments) or
+    "split" (sinkattn_decode_paged with the library's split count, then
+    sinkattn_merge).  The step time is that of the K steps captured in one
+    HIP graph and replayed (as a serving loop issues its decode steps); the
+    same steps issued one by one from Python are timed beside it; then each
+    of the two kernels is timed per launch.  The output returned is the
+    graph replay's."""
     import ctypes
     import gqa_attention_sinks_amd as sa
     from gqa_attention_sinks_amd import binding
     lib = sa.load_library()
     base = Dev(w, torch, dev)
     reps = [base] + [base.replica() for _ in range(max(0, args.replicas - 1))]
-    s = args.splits if args.splits > 0 else (w.num_splits or sa.pick_num_splits(w.kv_len, w.num_kv_heads))
     B, H, HKV = w.batch, w.num_qo_heads, w.num_kv_heads
     outs = [torch.empty_like(r.q) for r in reps]
-    o_part = torch.empty((B, H, s, 64), dtype=torch.float32, device=dev)
-    lse_part = torch.empty((B, H, s), dtype=torch.float32, device=dev)
     lses = [torch.empty((B, H), dtype=torch.float32, device=dev) for _ in reps]
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -423,30 +433,54 @@ def time_decode(w, args, torch, dev, window=0):
     sk = [P(r.sinks.data_ptr()) for r in reps]
     op = [P(o.data_ptr()) for o in outs]
     lp = [P(x.data_ptr()) for x in lses]
-    opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
     scale = ctypes.c_float(w.scale)
 
     def check(st):
         if st != 0:
             raise RuntimeError(lib.sinkattn_last_error().decode())
 
-    def decode_only(i, sp=sp):
-        r = i % len(reps)
-        if s > 1:
-            check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
-                                            B, H, HKV, 64, scale, window, sp))
-        else:
-            check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lp[r],
-                                            B, H, HKV, 64, scale, window, sp))
+    if mode == "balanced":
+        s = args.segments if args.segments > 0 else sa.pick_num_segments(HKV)
+        nbytes = sa.decode_balanced_workspace_bytes(B, H, s)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        wsp = P(ws.data_ptr())
 
-    def merge_only(i, sp=sp):
-        r = i % len(reps)
-        check(lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lp[r], sp))
+        def decode_only(i, sp=sp):
+            r = i % len(reps)
+            check(lib.sinkattn_decode_paged_balanced_pieces(qp[r], ctypes.byref(kvs[r]), sk[r], s, wsp, nbytes, op[r],
+                                                            lp[r], B, H, HKV, 64, scale, window, sp))
 
-    def step(i, sp=sp):
-        decode_only(i, sp)
-        if s > 1:
-            merge_only(i, sp)
+        def merge_only(i, sp=sp):
+            r = i % len(reps)
+            check(lib.sinkattn_merge_balanced(sk[r], s, wsp, nbytes, op[r], lp[r], B, H, 64, sp))
+
+        def step(i, sp=sp):
+            r = i % len(reps)
+            check(lib.sinkattn_decode_paged_balanced(qp[r], ctypes.byref(kvs[r]), sk[r], s, wsp, nbytes, op[r], lp[r],
+                                                     B, H, HKV, 64, scale, window, sp))
+    else:
+        s = args.splits if args.splits > 0 else (w.num_splits or sa.pick_num_splits(w.kv_len, w.num_kv_heads))
+        o_part = torch.empty((B, H, s, 64), dtype=torch.float32, device=dev)
+        lse_part = torch.empty((B, H, s), dtype=torch.float32, device=dev)
+        opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
+
+        def decode_only(i, sp=sp):
+            r = i % len(reps)
+            if s > 1:
+                check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], s, None, opart, lpart, None,
+                                                B, H, HKV, 64, scale, window, sp))
+            else:
+                check(lib.sinkattn_decode_paged(qp[r], ctypes.byref(kvs[r]), sk[r], 1, op[r], None, None, lp[r],
+                                                B, H, HKV, 64, scale, window, sp))
+
+        def merge_only(i, sp=sp):
+            r = i % len(reps)
+            check(lib.sinkattn_merge(opart, lpart, B, H, s, 64, op[r], lp[r], sp))
+
+        def step(i, sp=sp):
+            decode_only(i, sp)
+            if s > 1:
+                merge_only(i, sp)
 
     for i in range(args.warmup):
         step(i)
@@ -480,9 +514,9 @@ def time_decode(w, args, torch, dev, window=0):
     del graph
     n = max(args.steps, 200)
     dec = launch_times(decode_only, n, stream, torch)
-    mer = launch_times(merge_only, n, stream, torch) if s > 1 else [0.0]
+    mer = launch_times(merge_only, n, stream, torch) if (mode == "balanced" or s > 1) else [0.0]
     torch.cuda.synchronize()
-    return dict(step_ms=wall * 1e3, step_ms_eager=wall_eager * 1e3, decode=dec, merge=mer, splits=s,
+    return dict(step_ms=wall * 1e3, step_ms_eager=wall_eager * 1e3, decode=dec, merge=mer, splits=s, mode=mode,
                 out=out_host, lse=lse_host)
 
 
@@ -535,7 +569,8 @@ def measured_traffic(kernel, workload, splits):
         return None
     rec = json.load(open(path)).get(kernel)
     csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
-    files = [os.path.join(csrc, f) for f in ("decode.hip", "device_common.hpp", "kernel_args.hpp")]
+    src = "decode_balanced.hip" if kernel == "decode_balanced_kernel" else "decode.hip"
+    files = [os.path.join(csrc, f) for f in (src, "device_common.hpp", "kernel_args.hpp")]
     digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
     if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
             or rec.get("num_splits") != splits:
@@ -557,6 +592,8 @@ DESCR = {
     "long_split_decode": "long split decode: batch 8, 131072 keys each, 64 query / 8 KV heads, paged (page 16), "
                          "16 chunks with the sink in chunk 0 only, then the LSE merge; sinks N(0, 2) with -inf "
                          "and +20 outliers, seed 0",
+    "skewed_decode": "skewed decode (beyond the five workloads): batch 64, request 0 with 131072 keys, the others "
+                     "uniform in [1, 4096], 64 query / 8 KV heads, paged (page 16), sinks N(0, 2), seed 0",
     "mixed_batch": "mixed batch: 16 prefill chunks of 512 tokens on prefixes uniform in [0, 16384] + 240 decode "
                    "rows with KV lengths uniform in [1, 16384] in one call, 64 query / 8 KV heads, paged "
                    "(page 16), sinks N(0, 2), seed 0",
@@ -592,16 +629,20 @@ def leg_causal_prefill(w, args, torch, dev, oc):
             "cpu_baseline": oc.baselines.get("causal_prefill") if oc else None}
 
 
-def leg_decode(name, w, args, torch, dev, oc):
-    res = time_decode(w, args, torch, dev)
+def leg_decode(name, w, args, torch, dev, oc, mode):
+    res = time_decode(w, args, torch, dev, mode=mode)
     nbytes = decode_bytes(w)
     dst, mst = stats_ms(res["decode"]), stats_ms(res["merge"])
-    kernels = {"decode_paged_kernel": {"ms": dst, "algorithmic_bytes": nbytes,
-                                       "roofline": roofline_entry("decode_paged_kernel", "hbm", nbytes, dst["mean"])}}
-    if res["splits"] > 1:
+    kname = "decode_balanced_kernel" if mode == "balanced" else "decode_paged_kernel"
+    kernels = {kname: {"ms": dst, "algorithmic_bytes": nbytes,
+                       "roofline": roofline_entry(kname, "hbm", nbytes, dst["mean"])}}
+    if mode == "balanced":
+        kernels["merge_balanced_kernel"] = {"ms": mst}
+    elif res["splits"] > 1:
         part = 2 * w.batch * w.num_qo_heads * res["splits"] * (w.head_dim + 1) * 4
         kernels["merge_kernel"] = {"ms": mst, "partials_bytes": part}
-    entry = {"workload": DESCR[name], "bound": "hbm", "num_splits": res["splits"],
+    entry = {"workload": DESCR[name], "bound": "hbm", "decode_path": mode,
+             ("num_segments" if mode == "balanced" else "num_splits"): res["splits"],
              "step_ms_graph": round(res["step_ms"], 5), "step_ms_eager": round(res["step_ms_eager"], 5),
              "step_GBs": round(nbytes / (res["step_ms"] * 1e-3) / 1e9, 1),
              "kernels": kernels,
@@ -691,7 +732,7 @@ def main():
     t_start = time.perf_counter()
     log("generating workloads")
     ws = {n: getattr(wl, n)() for n in ["tiny_prefill", "paged_decode", "causal_prefill", "long_split_decode",
-                                         "mixed_batch"]}
+                                         "mixed_batch", "skewed_decode"]}
     cores = len(os.sched_getaffinity(0))
     oc = None
     if not args.no_cpu:
@@ -709,9 +750,11 @@ def main():
     dev = torch.device("cuda:0")
 
     configs = {}
-    log("paged_decode")
-    head, res = leg_decode("paged_decode", ws["paged_decode"], args, torch, dev, oc)
+    other = "split" if args.decode == "balanced" else "balanced"
+    log(f"paged_decode ({args.decode}, then {other})")
+    head, res = leg_decode("paged_decode", ws["paged_decode"], args, torch, dev, oc, args.decode)
     configs["paged_decode"] = head
+    configs[f"paged_decode_{other}"], _ = leg_decode("paged_decode", ws["paged_decode"], args, torch, dev, oc, other)
     torch.cuda.empty_cache()
     log("tiny_prefill")
     configs["tiny_prefill"] = leg_tiny(ws["tiny_prefill"], args, torch, dev, oc)
@@ -720,7 +763,15 @@ def main():
     torch.cuda.empty_cache()
     log("long_split_decode")
     configs["long_split_decode"], _ = leg_decode("long_split_decode", ws["long_split_decode"], args, torch,
-                                                 dev, oc)
+                                                 dev, oc, "split")
+    configs["long_split_decode_balanced"], _ = leg_decode("long_split_decode", ws["long_split_decode"], args,
+                                                          torch, dev, oc, "balanced")
+    torch.cuda.empty_cache()
+    log("skewed_decode")
+    configs["skewed_decode_balanced"], _ = leg_decode("skewed_decode", ws["skewed_decode"], args, torch, dev, oc,
+                                                      "balanced")
+    configs["skewed_decode_split"], _ = leg_decode("skewed_decode", ws["skewed_decode"], args, torch, dev, oc,
+                                                   "split")
     torch.cuda.empty_cache()
     for window in (128, 0):
         log(f"mixed_batch window={window}")
@@ -731,9 +782,11 @@ def main():
     w = ws["paged_decode"]
     nbytes = decode_bytes(w)
     value = nbytes / (res["step_ms"] * 1e-3) / 1e9
-    dmean = head["kernels"]["decode_paged_kernel"]["ms"]["mean"]
-    roof = roofline_entry("decode_paged_kernel", "hbm", nbytes, dmean,
-                          measured_traffic("decode_paged_kernel", "paged_decode", res["splits"]))
+    kname = "decode_balanced_kernel" if args.decode == "balanced" else "decode_paged_kernel"
+    mname = "merge_balanced_kernel" if args.decode == "balanced" else "merge_kernel"
+    dmean = head["kernels"][kname]["ms"]["mean"]
+    roof = roofline_entry(kname, "hbm", nbytes, dmean,
+                          measured_traffic(kname, "paged_decode", res["splits"]))
     pre = configs["causal_prefill"]["kernels"]["prefill_kernel"]
     line = {
         "metric": METRIC,
@@ -750,14 +803,15 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": DESCR["paged_decode"],
-            "num_splits": res["splits"],
+            "decode_path": args.decode,
+            ("num_segments" if args.decode == "balanced" else "num_splits"): res["splits"],
             "kv_replicas_rotated": args.replicas,
             "algorithmic_bytes": nbytes,
             "compute": "bf16 Q.K^T and fp16 P.V on MFMA, fp32 accumulation",
             "step": "K steps (decode + merge launches) captured in one HIP graph, replayed",
             "ms_per_step_eager": round(res["step_ms_eager"], 5),
-            "decode_kernel_ms": head["kernels"]["decode_paged_kernel"]["ms"],
-            "merge_kernel_ms": head["kernels"].get("merge_kernel", {}).get("ms"),
+            "decode_kernel_ms": head["kernels"][kname]["ms"],
+            "merge_kernel_ms": head["kernels"].get(mname, {}).get("ms"),
             "pct_hbm_peak_step": round(100 * value / HBM_PEAK_GBS, 2),
         },
         "roofline": roof,
@@ -933,8 +987,8 @@ def profile_only(args):
                           "step_ms": res["step_ms"], "decode_ms": res["decode"], "decode_GBs": gbs,
                           "frac": gbs / HBM_PEAK_GBS}))
         return
-    if name in ("paged_decode", "long_split_decode"):
-        entry, _ = leg_decode(name, w, args, torch, dev, None)
+    if name in ("paged_decode", "long_split_decode", "skewed_decode"):
+        entry, _ = leg_decode(name, w, args, torch, dev, None, args.decode)
         print(json.dumps({"workload": name, **entry}))
         return
     if name == "tiny_prefill":

@@ -12,7 +12,12 @@ from .binding import (  # noqa: F401
     SinkAttnError,
     abi_version,
     append_paged_kv_rope,
+    balanced_segments,
+    balanced_workspace_segments,
+    balanced_workspace_views,
+    decode_balanced_workspace_bytes,
     decode_paged,
+    decode_paged_balanced,
     decode_paged_multi,
     decode_paged_noalloc,
     kv_descriptor,
@@ -20,6 +25,7 @@ from .binding import (  # noqa: F401
     load_library,
     merge,
     moe_topk_softmax,
+    pick_num_segments,
     pick_num_splits,
     pick_num_splits_multi,
     prefill,

@@ -23,11 +23,18 @@ MAX_SPLITS = 256
 MAX_DECODE_ROWS = 8
 MAX_EXPERTS = 512
 MAX_TOP_K = 8
+MAX_BALANCED_BATCH = 256
 NOALLOC_SCRATCH_BYTES = 8 << 20
 EXPORTED = (
     "sinkattn_prefill",
     "sinkattn_decode_paged",
     "sinkattn_decode_paged_noalloc",
+    "sinkattn_decode_paged_balanced",
+    "sinkattn_decode_paged_balanced_pieces",
+    "sinkattn_merge_balanced",
+    "sinkattn_decode_balanced_workspace_bytes",
+    "sinkattn_pick_num_segments",
+    "sinkattn_balanced_segments",
     "sinkattn_decode_paged_multi",
     "sinkattn_append_paged_kv_rope",
     "sinkattn_moe_topk_softmax",
@@ -88,6 +95,19 @@ def load_library():
     lib.sinkattn_decode_paged_noalloc.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, vp, i32, i32, i32, i32,
                                                   f32, i32, vp]
     lib.sinkattn_decode_paged_noalloc.restype = i32
+    lib.sinkattn_decode_paged_balanced.argtypes = [vp, ctypes.POINTER(_KV), vp, i32, vp, ctypes.c_int64, vp, vp,
+                                                   i32, i32, i32, i32, f32, i32, vp]
+    lib.sinkattn_decode_paged_balanced.restype = i32
+    lib.sinkattn_decode_paged_balanced_pieces.argtypes = lib.sinkattn_decode_paged_balanced.argtypes
+    lib.sinkattn_decode_paged_balanced_pieces.restype = i32
+    lib.sinkattn_merge_balanced.argtypes = [vp, i32, vp, ctypes.c_int64, vp, vp, i32, i32, i32, vp]
+    lib.sinkattn_merge_balanced.restype = i32
+    lib.sinkattn_decode_balanced_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.sinkattn_decode_balanced_workspace_bytes.restype = ctypes.c_int64
+    lib.sinkattn_pick_num_segments.argtypes = [i32]
+    lib.sinkattn_pick_num_segments.restype = i32
+    lib.sinkattn_balanced_segments.argtypes = [vp, i32, i32, i32, vp]
+    lib.sinkattn_balanced_segments.restype = i32
     lib.sinkattn_decode_paged_multi.argtypes = [vp, vp, vp, vp, ctypes.POINTER(_KV), vp, i32, vp, vp, vp,
                                                 vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     lib.sinkattn_decode_paged_multi.restype = i32
@@ -306,6 +326,84 @@ def decode_paged_noalloc(q, k_pool, v_pool, page_indptr, page_indices, kv_len, s
                                              _ptr(lse), batch, hq, k_pool.shape[1], HEAD_DIM, float(sm_scale),
                                              int(window), _stream(stream)))
     return (out, lse) if (return_lse or lse is not None) else out
+
+
+def decode_balanced_workspace_bytes(batch: int, num_qo_heads: int, num_segments: int) -> int:
+    """Bytes of workspace :func:`decode_paged_balanced` needs."""
+    n = int(load_library().sinkattn_decode_balanced_workspace_bytes(batch, num_qo_heads, num_segments))
+    if n < 0:
+        raise ValueError("batch, num_qo_heads and num_segments must be >= 1")
+    return n
+
+
+def pick_num_segments(num_kv_heads: int) -> int:
+    """Host-only segment count that fills the current GPU in one launch round."""
+    return int(load_library().sinkattn_pick_num_segments(int(num_kv_heads)))
+
+
+def balanced_segments(kv_len_host, num_segments: int, window: int = 0) -> np.ndarray:
+    """Host-only segment rule of the balanced decode: int32 [B, 2] first and
+    last segment of each request (-1 for a request without keys)."""
+    lens = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+    out = np.zeros((len(lens), 2), dtype=np.int32)
+    _check(load_library().sinkattn_balanced_segments(lens.ctypes.data_as(ctypes.c_void_p), len(lens), int(window),
+                                                     int(num_segments), out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def decode_paged_balanced(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm_scale: float,
+                          num_segments: int = 0, window: int = 0, out=None, lse=None, workspace=None,
+                          return_lse: bool = False, stream=None):
+    """``sinkattn_decode_paged_balanced``: one query token per request, the
+    batch's live pages cut into ``num_segments`` equal segments (0: the
+    library's pick).  ``workspace`` (uint8 device tensor) is allocated here
+    when not given.  Returns ``out`` (and ``lse``)."""
+    torch = _torch()
+    _dev(q, "q", torch.bfloat16)
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM:
+        raise ValueError("q must be [batch, Hq, 64]")
+    batch, hq, _ = q.shape
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    hkv = k_pool.shape[1]
+    if sinks is not None:
+        _dev(sinks, "sinks", torch.float32, (hq,))
+    n_seg = int(num_segments) if num_segments else pick_num_segments(hkv)
+    need = decode_balanced_workspace_bytes(batch, hq, n_seg)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _dev(workspace, "workspace", torch.uint8)
+    if out is None:
+        out = torch.empty_like(q)
+    _dev(out, "out", torch.bfloat16, q.shape)
+    if return_lse and lse is None:
+        lse = torch.empty((batch, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _dev(lse, "lse", torch.float32, (batch, hq))
+    lib = load_library()
+    _check(lib.sinkattn_decode_paged_balanced(_ptr(q), ctypes.byref(kvs), _ptr(sinks), n_seg, _ptr(workspace),
+                                              workspace.numel(), _ptr(out), _ptr(lse), batch, hq, hkv, HEAD_DIM,
+                                              float(sm_scale), int(window), _stream(stream)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+def balanced_workspace_views(workspace, batch: int, num_qo_heads: int, num_segments: int):
+    """The documented parts of a balanced-decode workspace: (plan int32
+    [B+1], lse fp32 [slots, Hq], o fp32 [slots, Hq, 64]), slots =
+    num_segments + batch; the segment table int32 [B, 2] follows the plan
+    (``balanced_workspace_segments``)."""
+    slots = num_segments + batch
+    plan_bytes = ((3 * batch + 1) * 4 + 255) // 256 * 256
+    lse_bytes = (slots * num_qo_heads * 4 + 255) // 256 * 256
+    plan = workspace[:(batch + 1) * 4].view(_torch().int32)
+    lse = workspace[plan_bytes:plan_bytes + slots * num_qo_heads * 4].view(_torch().float32)
+    o = workspace[plan_bytes + lse_bytes:plan_bytes + lse_bytes + slots * num_qo_heads * HEAD_DIM * 4]
+    return plan, lse.view(slots, num_qo_heads), o.view(_torch().float32).view(slots, num_qo_heads, HEAD_DIM)
+
+
+def balanced_workspace_segments(workspace, batch: int):
+    """The segment table of a balanced-decode workspace: int32 [B, 2], each
+    request's first and last segment (-1 for a request without keys)."""
+    return workspace[(batch + 1) * 4:(3 * batch + 1) * 4].view(_torch().int32).view(batch, 2)
 
 
 def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks,

@@ -262,6 +262,150 @@ sinkattn_status sinkattn_decode_paged_noalloc(const void* q, const sinkattn_kv* 
                                num_kv_heads, head_dim, sm_scale, window, stream);
 }
 
+int64_t sinkattn_decode_balanced_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t num_segments) {
+  if (batch < 1 || num_qo_heads < 1 || num_segments < 1) return -1;
+  const int64_t slots = (int64_t)num_segments + batch;
+  const int64_t plan = ((int64_t)(3 * batch + 1) * 4 + 255) & ~(int64_t)255;
+  const int64_t lse = (slots * num_qo_heads * 4 + 255) & ~(int64_t)255;
+  return plan + lse + slots * num_qo_heads * SINKATTN_HEAD_DIM * 4;
+}
+
+int32_t sinkattn_pick_num_segments(int32_t num_kv_heads) {
+  if (num_kv_heads < 1) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 256;
+  const int32_t n = (cus * sinkattn::kBalancedWavesPerSimd + num_kv_heads - 1) / num_kv_heads;
+  return n > 1 ? n : 1;
+}
+
+sinkattn_status sinkattn_balanced_segments(const int32_t* kv_len_host, int32_t batch, int32_t window,
+                                           int32_t num_segments, int32_t* segs_host) {
+  REQUIRE(kv_len_host != nullptr && segs_host != nullptr, SINKATTN_ERR_INVALID_ARG,
+          "kv_len_host and segs_host are required");
+  REQUIRE(batch >= 0, SINKATTN_ERR_INVALID_ARG, "batch must be >= 0");
+  REQUIRE(window >= 0, SINKATTN_ERR_INVALID_ARG, "window must be >= 0");
+  REQUIRE(num_segments >= 1 && num_segments <= 65536, SINKATTN_ERR_INVALID_ARG,
+          "num_segments must be in [1, 65536]");
+  int64_t total = 0;
+  for (int32_t b = 0; b < batch; ++b) {
+    REQUIRE(kv_len_host[b] >= 0, SINKATTN_ERR_INVALID_ARG, "kv_len[%d] < 0", b);
+    const int64_t n_k = kv_len_host[b];
+    const int64_t lo = window > 0 ? (n_k - window > 0 ? n_k - window : 0) : 0;
+    total += n_k > 0 ? (n_k + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE - lo / SINKATTN_PAGE_SIZE : 0;
+  }
+  int64_t pos = 0;   // list position of the request's first live page
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t n_k = kv_len_host[b];
+    const int64_t lo = window > 0 ? (n_k - window > 0 ? n_k - window : 0) : 0;
+    const int64_t n = n_k > 0 ? (n_k + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE - lo / SINKATTN_PAGE_SIZE : 0;
+    // list position f lies in segment floor(((f + 1) N - 1) / T)
+    segs_host[2 * b] = n > 0 ? (int32_t)(((pos + 1) * num_segments - 1) / total) : -1;
+    segs_host[2 * b + 1] = n > 0 ? (int32_t)(((pos + n) * num_segments - 1) / total) : -1;
+    pos += n;
+  }
+  return SINKATTN_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Arguments of the balanced decode's launches, checked; `need_kv`: the
+// pieces launch (the merge reads only the workspace, sinks and outputs).
+sinkattn_status balanced_args(const void* q, const sinkattn_kv* kv, const float* sinks, int32_t num_segments,
+                              const void* workspace, int64_t workspace_bytes, void* out, float* lse,
+                              int32_t batch, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                              float sm_scale, int32_t window, bool need_kv, sinkattn::BalancedArgs* a) {
+  REQUIRE(out != nullptr && workspace != nullptr, SINKATTN_ERR_INVALID_ARG, "out and workspace are required");
+  sinkattn_status st = check_heads(batch, num_qo_heads, num_kv_heads, head_dim, sm_scale, window);
+  if (st != SINKATTN_OK) return st;
+  if (need_kv) {
+    REQUIRE(q != nullptr, SINKATTN_ERR_INVALID_ARG, "q is required");
+    if ((st = check_kv(kv, true)) != SINKATTN_OK) return st;
+  }
+  REQUIRE(batch <= SINKATTN_MAX_BALANCED_BATCH, SINKATTN_ERR_UNSUPPORTED,
+          "batch %d above %d: use sinkattn_decode_paged", batch, SINKATTN_MAX_BALANCED_BATCH);
+  REQUIRE(num_segments >= 1 && num_segments <= 65536, SINKATTN_ERR_INVALID_ARG,
+          "num_segments must be in [1, 65536] (got %d)", num_segments);
+  REQUIRE(((uintptr_t)workspace & 15) == 0, SINKATTN_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const int64_t need = sinkattn_decode_balanced_workspace_bytes(batch, num_qo_heads, num_segments);
+  REQUIRE(workspace_bytes >= need, SINKATTN_ERR_INVALID_ARG, "workspace of %lld bytes, %lld needed",
+          (long long)workspace_bytes, (long long)need);
+  REQUIRE((long)num_segments * num_kv_heads < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  const int64_t slots = (int64_t)num_segments + batch;
+  unsigned char* ws = static_cast<unsigned char*>(const_cast<void*>(workspace));
+  const int64_t plan_bytes = ((int64_t)(3 * batch + 1) * 4 + 255) & ~(int64_t)255;
+  const int64_t lse_bytes = (slots * num_qo_heads * 4 + 255) & ~(int64_t)255;
+  *a = sinkattn::BalancedArgs{};
+  a->q = static_cast<const uint16_t*>(q);
+  if (need_kv) {
+    a->k_pool = static_cast<const uint16_t*>(kv->k);
+    a->v_pool = static_cast<const uint16_t*>(kv->v);
+    a->page_indptr = kv->kv_indptr;
+    a->page_indices = kv->page_indices;
+    a->kv_len = kv->kv_len;
+  }
+  a->sinks = sinks;
+  a->out = static_cast<uint16_t*>(out);
+  a->lse = lse;
+  a->ws_plan = reinterpret_cast<int32_t*>(ws);
+  a->ws_seg = a->ws_plan + batch + 1;
+  a->ws_lse = reinterpret_cast<float*>(ws + plan_bytes);
+  a->ws_o = reinterpret_cast<float*>(ws + plan_bytes + lse_bytes);
+  a->scale_log2 = sm_scale * 1.4426950408889634f;
+  a->batch = batch;
+  a->num_qo_heads = num_qo_heads;
+  a->num_kv_heads = num_kv_heads;
+  a->group = num_qo_heads / num_kv_heads;
+  a->window = window;
+  a->num_segments = num_segments;
+  return SINKATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sinkattn_status sinkattn_decode_paged_balanced_pieces(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                                      int32_t num_segments, void* workspace,
+                                                      int64_t workspace_bytes, void* out, float* lse,
+                                                      int32_t batch, int32_t num_qo_heads,
+                                                      int32_t num_kv_heads, int32_t head_dim,
+                                                      float sm_scale, int32_t window, void* stream) {
+  sinkattn::BalancedArgs a;
+  sinkattn_status st = balanced_args(q, kv, sinks, num_segments, workspace, workspace_bytes, out, lse, batch,
+                                     num_qo_heads, num_kv_heads, head_dim, sm_scale, window, true, &a);
+  if (st != SINKATTN_OK) return st;
+  return hip_status(sinkattn::launch_decode_balanced(a, static_cast<hipStream_t>(stream)), "balanced decode launch");
+}
+
+sinkattn_status sinkattn_merge_balanced(const float* sinks, int32_t num_segments, const void* workspace,
+                                        int64_t workspace_bytes, void* out, float* lse, int32_t batch,
+                                        int32_t num_qo_heads, int32_t head_dim, void* stream) {
+  sinkattn::BalancedArgs a;
+  sinkattn_status st = balanced_args(nullptr, nullptr, sinks, num_segments, workspace, workspace_bytes, out, lse,
+                                     batch, num_qo_heads, num_qo_heads, head_dim, 1.f, 0, false, &a);
+  if (st != SINKATTN_OK) return st;
+  return hip_status(sinkattn::launch_merge_balanced(a, static_cast<hipStream_t>(stream)), "balanced merge launch");
+}
+
+sinkattn_status sinkattn_decode_paged_balanced(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                               int32_t num_segments, void* workspace,
+                                               int64_t workspace_bytes, void* out, float* lse,
+                                               int32_t batch, int32_t num_qo_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                               int32_t window, void* stream) {
+  sinkattn::BalancedArgs a;
+  sinkattn_status st = balanced_args(q, kv, sinks, num_segments, workspace, workspace_bytes, out, lse, batch,
+                                     num_qo_heads, num_kv_heads, head_dim, sm_scale, window, true, &a);
+  if (st != SINKATTN_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = hip_status(sinkattn::launch_decode_balanced(a, s), "balanced decode launch")) != SINKATTN_OK) return st;
+  return hip_status(sinkattn::launch_merge_balanced(a, s), "balanced merge launch");
+}
+
 sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_indptr,
                                             const uint8_t* custom_mask, const int32_t* mask_indptr,
                                             const sinkattn_kv* kv, const float* sinks,

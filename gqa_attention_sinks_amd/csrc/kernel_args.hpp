@@ -61,6 +61,28 @@ struct PrefillArgs {
   int32_t num_slots;          // tile slots launched (upper bound on tiles)
 };
 
+// Balanced split decode: the batch's live pages cut into equal segments; see
+// sinkattn_decode_paged_balanced in include/sinkattn.h.
+constexpr int kBalancedMaxBatch = 256;     // the plan of a launch is built in LDS
+constexpr int kBalancedWavesPerSimd = 6;   // 4-wave workgroups: six per CU at a time
+struct BalancedArgs {
+  const uint16_t* q;          // [B, Hq, 64] bf16
+  const uint16_t* k_pool;     // [num_pages, Hkv, 16, 64] bf16
+  const uint16_t* v_pool;
+  const int32_t* page_indptr; // [B+1]
+  const int32_t* page_indices;
+  const int32_t* kv_len;      // [B]
+  const float* sinks;         // [Hq] or null
+  uint16_t* out;              // [B, Hq, 64] bf16
+  float* lse;                 // optional [B, Hq]
+  int32_t* ws_plan;           // workspace: [B+1] live-page prefix (written by workgroup 0)
+  int32_t* ws_seg;            // workspace: [B][2] first and last segment of each request (-1: no key)
+  float* ws_lse;              // workspace: [slots, Hq] partial LSE (natural log), slot = segment + request
+  float* ws_o;                // workspace: [slots, Hq, 64] partial outputs
+  float scale_log2;
+  int32_t batch, num_qo_heads, num_kv_heads, group, window, num_segments;
+};
+
 // Paged KV append with rotary embedding of the new queries and keys; see
 // sinkattn_append_paged_kv_rope in include/sinkattn.h.
 struct AppendArgs {
@@ -87,6 +109,8 @@ struct MoeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream);   // pieces
+hipError_t launch_merge_balanced(const BalancedArgs& a, hipStream_t stream);
 hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream);
 hipError_t launch_append_rope(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);

@@ -225,6 +225,18 @@ def paged_decode(seed=0, batch=64, max_len=4096, num_qo_heads=64, num_kv_heads=8
                       rng=rng, decode=True)
 
 
+def skewed_decode(seed=0, batch=64, long_len=131072, max_len=4096, num_qo_heads=64, num_kv_heads=8) -> Workload:
+    """A decode batch with one very long request: request 0 holds 131072 keys,
+    the other 63 hold KV lengths uniform in [1, 4096]; 64/8 heads, page size
+    16, permuted shared pool, sinks N(0, 2).  A split into a fixed number of
+    chunks per request leaves the long request to a few workgroups; the
+    balanced split does not."""
+    rng = np.random.default_rng(seed)
+    kv_len = rng.integers(1, max_len + 1, size=batch)
+    kv_len[0] = long_len
+    return make_paged("skewed_decode", kv_len, np.ones(batch), num_qo_heads, num_kv_heads, rng=rng, decode=True)
+
+
 def causal_prefill(seed=0, batch=4, seq=8192, num_qo_heads=64, num_kv_heads=8) -> Workload:
     """4 sequences of 8192 tokens, full causal, 64/8 heads, contiguous KV,
     scale 1/sqrt(64), sinks N(0, 2)."""
@@ -332,6 +344,7 @@ def pack_masks(masks):
 NAMED = {
     "tiny_prefill": tiny_prefill,
     "paged_decode": paged_decode,
+    "skewed_decode": skewed_decode,
     "causal_prefill": causal_prefill,
     "long_split_decode": long_split_decode,
     "mixed_batch": mixed_batch,

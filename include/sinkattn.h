@@ -78,6 +78,7 @@ extern "C" {
 #define SINKATTN_MAX_DECODE_ROWS 8
 #define SINKATTN_MAX_EXPERTS 512
 #define SINKATTN_MAX_TOP_K 8
+#define SINKATTN_MAX_BALANCED_BATCH 256
 #define SINKATTN_NOALLOC_SCRATCH_BYTES (8u << 20) /* partials of sinkattn_decode_paged_noalloc */
 
 typedef enum {
@@ -167,6 +168,82 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
                                       int32_t num_qo_heads, int32_t num_kv_heads,
                                       int32_t head_dim, float sm_scale, int32_t window,
                                       void* stream);
+
+/* One query token per request over a paged KV cache, the batch's work split
+ * into equal segments: the same results as sinkattn_decode_paged (out, lse),
+ * computed with a split that does not depend on the mix of request lengths.
+ * "GPT-OSS on day 0", section "Kernels for GPT-OSS > Sink attention": the
+ * attention is split into blocks along the KV sequence, only the first block
+ * of a request carries its sink, and the blocks' partial softmaxes are
+ * merged.  The blocks: a request's live pages are those holding the keys its
+ * query row sees (keys max(0, n_k - window) .. n_k - 1; all keys when window
+ * == 0); the batch's live pages, request after request, form one list of T
+ * pages, and segment s (0 <= s < num_segments) holds list positions
+ * [floor(s T / N), floor((s + 1) T / N)).  A request's part of a segment is
+ * one block.  One workgroup per (segment, KV head) walks its segment; a
+ * request that lies in one segment is finished there, the blocks of the
+ * others are merged by a second launch.
+ *   q            [batch, Hq, 64] bf16; the query of request b sits at position
+ *                kv_len[b] - 1
+ *   kv           paged descriptor (kv->paged must be 1)
+ *   num_segments 1 .. 65536; sinkattn_pick_num_segments gives the count that
+ *                fills the GPU once
+ *   workspace    device memory of at least
+ *                sinkattn_decode_balanced_workspace_bytes(batch, Hq,
+ *                num_segments) bytes, 16-byte aligned, owned by the caller;
+ *                its contents on entry do not matter.  On return it holds
+ *                int32 plan[batch + 1] (the live-page prefix: request b owns
+ *                list positions plan[b] .. plan[b+1] - 1) and int32
+ *                seg[batch][2] (each request's first and last segment, -1
+ *                for a request without keys), then (at the next multiple of
+ *                256 bytes) fp32 lse[slots][Hq], then fp32
+ *                o[slots][Hq][64], slots = num_segments + batch: the blocks of
+ *                the requests that span several segments, request b's block
+ *                in segment s at slot s + b, each normalised by its own
+ *                denominator with its natural-log LSE (the first block with
+ *                the sink).  Calls that share a workspace must not overlap.
+ *   out          [batch, Hq, 64] bf16, written; lse optional [batch, Hq] fp32
+ * batch <= SINKATTN_MAX_BALANCED_BATCH (the plan of a launch is built in the
+ * workgroups' shared memory); larger batches get SINKATTN_ERR_UNSUPPORTED and
+ * are served by sinkattn_decode_paged.  A request with no key gets out = 0,
+ * lse = sink. */
+sinkattn_status sinkattn_decode_paged_balanced(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                               int32_t num_segments, void* workspace,
+                                               int64_t workspace_bytes, void* out, float* lse,
+                                               int32_t batch, int32_t num_qo_heads,
+                                               int32_t num_kv_heads, int32_t head_dim, float sm_scale,
+                                               int32_t window, void* stream);
+
+/* The two launches of sinkattn_decode_paged_balanced one at a time (same
+ * arguments and contract): _pieces walks the segments (requests that lie in
+ * one segment get their out and lse; the others leave their blocks in the
+ * workspace), then _merge (with the workspace of that call) merges those
+ * blocks into out and lse and writes the requests without keys.  For callers
+ * that time or schedule the two apart. */
+sinkattn_status sinkattn_decode_paged_balanced_pieces(const void* q, const sinkattn_kv* kv, const float* sinks,
+                                                      int32_t num_segments, void* workspace,
+                                                      int64_t workspace_bytes, void* out, float* lse,
+                                                      int32_t batch, int32_t num_qo_heads,
+                                                      int32_t num_kv_heads, int32_t head_dim,
+                                                      float sm_scale, int32_t window, void* stream);
+sinkattn_status sinkattn_merge_balanced(const float* sinks, int32_t num_segments, const void* workspace,
+                                        int64_t workspace_bytes, void* out, float* lse, int32_t batch,
+                                        int32_t num_qo_heads, int32_t head_dim, void* stream);
+
+/* Host-only: bytes of workspace sinkattn_decode_paged_balanced needs (-1 on
+ * invalid arguments). */
+int64_t sinkattn_decode_balanced_workspace_bytes(int32_t batch, int32_t num_qo_heads, int32_t num_segments);
+
+/* Host-only: the segment count for sinkattn_decode_paged_balanced that lets
+ * every (segment, KV head) workgroup of one launch run at once on the current
+ * device (six per compute unit). */
+int32_t sinkattn_pick_num_segments(int32_t num_kv_heads);
+
+/* Host-only: the segment rule of sinkattn_decode_paged_balanced, for callers
+ * and tests.  kv_len_host [batch] (host); segs_host [batch, 2] (host) receives
+ * each request's first and last segment (-1, -1 for a request without keys). */
+sinkattn_status sinkattn_balanced_segments(const int32_t* kv_len_host, int32_t batch, int32_t window,
+                                           int32_t num_segments, int32_t* segs_host);
 
 /* sinkattn_decode_paged for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

@@ -342,3 +342,57 @@ def test_noalloc_rejects_partials_beyond_its_scratch(lib):
     assert f(FAKE, ctypes.byref(kv), None, 0, FAKE, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0, None) == INVALID
     assert f(FAKE, ctypes.byref(_kv(paged=0)), None, 2, FAKE, None, 2, 8, 2, 64, ctypes.c_float(0.125), 0,
              None) == INVALID
+
+
+# ---------------------------------------------------------------------------
+# the balanced decode's host side
+# ---------------------------------------------------------------------------
+
+def test_balanced_segment_rule_matches_oracle_exactly(lib):
+    rng = np.random.default_rng(77)
+    for _ in range(2000):
+        batch = int(rng.integers(1, 70))
+        lens = rng.integers(0, 5000, size=batch)
+        lens[rng.random(batch) < 0.1] = 0
+        window = int(rng.choice([0, 0, 1, 16, 100, 3000]))
+        n = int(rng.integers(1, 400))
+        got = sa.balanced_segments(lens, n, window)
+        ref = np.array([[p[0][0], p[-1][0]] for p in oracle.balanced_pieces_ref(lens, n, window)])
+        np.testing.assert_array_equal(got, ref)
+
+
+def test_balanced_workspace_bytes(lib):
+    # plan [B+1] and segments [B, 2] int32, lse [slots, Hq] fp32, each padded to 256 bytes, then
+    # o [slots, Hq, 64] fp32
+    b, hq, n = 64, 64, 192
+    slots = n + b
+    expect = 1024 + (slots * hq * 4 + 255) // 256 * 256 + slots * hq * 64 * 4
+    assert sa.decode_balanced_workspace_bytes(b, hq, n) == expect
+    assert lib.sinkattn_decode_balanced_workspace_bytes(0, 64, 4) == -1
+    assert 1 <= sa.pick_num_segments(8) <= 65536
+
+
+def _balanced(lib, kv, n=4, ws=FAKE, ws_bytes=1 << 30, out=FAKE, batch=2, hq=8, hkv=2, d=64, window=0, q=FAKE):
+    return lib.sinkattn_decode_paged_balanced(q, ctypes.byref(kv) if kv is not None else None, None, n, ws, ws_bytes,
+                                              out, None, batch, hq, hkv, d, ctypes.c_float(0.125), window, None)
+
+
+@pytest.mark.parametrize("kwargs,code", [
+    (dict(q=None), INVALID),
+    (dict(out=None), INVALID),
+    (dict(ws=None), INVALID),
+    (dict(ws=ctypes.c_void_p(0x1008)), INVALID),       # workspace not 16-byte aligned
+    (dict(ws_bytes=1000), INVALID),                     # too small
+    (dict(n=0), INVALID),
+    (dict(batch=257), UNSUPPORTED),
+    (dict(d=128), UNSUPPORTED),
+    (dict(window=-1), INVALID),
+])
+def test_balanced_argument_errors(lib, kwargs, code):
+    assert _balanced(lib, _kv(), **kwargs) == code
+    assert lib.sinkattn_last_error()
+
+
+def test_balanced_needs_paged(lib):
+    assert _balanced(lib, _kv(paged=0)) == INVALID
+    assert lib.sinkattn_merge_balanced(None, 4, None, 1 << 20, FAKE, None, 2, 8, 64, None) == INVALID

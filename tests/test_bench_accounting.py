@@ -102,10 +102,11 @@ def test_oracle_legs_cover_the_rows_they_claim():
                                                   num_kv_heads=2),
         "mixed_batch": wl.mixed_batch(n_prefill=3, chunk=40, max_prefix=100, n_decode=5, max_decode_len=300,
                                       num_qo_heads=8, num_kv_heads=2),
+        "skewed_decode": wl.skewed_decode(batch=5, long_len=900, max_len=100, num_qo_heads=8, num_kv_heads=2),
     }
     oc = bench.run_oracles(ws, 3)
     assert set(oc.baselines) == {"tiny_prefill", "paged_decode", "causal_prefill", "long_split_decode",
-                                 "mixed_batch_w128", "mixed_batch_full"}
+                                 "mixed_batch_w128", "mixed_batch_full", "skewed_decode"}
     for name, b in oc.baselines.items():
         assert b["kind"] == "oracle" and b["value"] > 0 and 1 <= b["cores"] <= 3, name
 
@@ -116,7 +117,8 @@ def test_oracle_legs_cover_the_rows_they_claim():
 
     for name, key, window in [("tiny_prefill", "tiny_prefill", 0), ("paged_decode", "paged_decode", 0),
                               ("causal_prefill", "causal_prefill", 0), ("long_split_decode", "long_split_decode", 0),
-                              ("mixed_batch_w128", "mixed_batch", 128), ("mixed_batch_full", "mixed_batch", 0)]:
+                              ("mixed_batch_w128", "mixed_batch", 128), ("mixed_batch_full", "mixed_batch", 0),
+                              ("skewed_decode", "skewed_decode", 0)]:
         w = ws[key]
         out, lse = whole(w, window)
         # the oracle's own results pass through the parity summary exactly

@@ -569,8 +569,8 @@ def measured_traffic(kernel, workload, splits):
         return None
     rec = json.load(open(path)).get(kernel)
     csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
-    src = "decode_balanced.hip" if kernel == "decode_balanced_kernel" else "decode.hip"
-    files = [os.path.join(csrc, f) for f in (src, "device_common.hpp", "kernel_args.hpp")]
+    srcs = (("decode_balanced.hip",) if kernel == "decode_balanced_kernel" else ("decode.hip", "decode_common.hpp"))
+    files = [os.path.join(csrc, f) for f in (*srcs, "device_common.hpp", "kernel_args.hpp")]
     digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
     if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
             or rec.get("num_splits") != splits:

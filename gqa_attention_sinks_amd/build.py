@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libsinkattn.so")
-SOURCES = ["api.hip", "append.hip", "decode.hip", "decode_balanced.hip", "moe.hip", "prefill.hip"]
+SOURCES = ["api.hip", "append.hip", "decode.hip", "decode_balanced.hip", "moe.hip", "prefill.hip", "verify.hip"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU forms are switched off for all device code.
@@ -33,7 +33,7 @@ FLAGS = [
 # -inf and rows past the last key are zero-filled), so max chains compile to
 # v_max3 without NaN canonicalisation.  The host validation in api.hip keeps
 # full NaN semantics (it must reject a NaN softmax scale).
-KERNEL_SOURCES = {"append.hip", "decode.hip", "decode_balanced.hip", "moe.hip", "prefill.hip"}
+KERNEL_SOURCES = {"append.hip", "decode.hip", "decode_balanced.hip", "moe.hip", "prefill.hip", "verify.hip"}
 KERNEL_FLAGS = ["-fno-honor-nans"]
 
 

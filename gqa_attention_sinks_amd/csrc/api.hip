@@ -462,7 +462,7 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
   d.window = window;
   d.max_rows = max_qo_len;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
+  if ((st = hip_status(sinkattn::launch_decode_verify(d, s), "verify decode launch")) != SINKATTN_OK) return st;
   if (num_splits > 1 && out != nullptr) {
     sinkattn::MergeArgs m{o_part, lse_part, static_cast<uint16_t*>(out), lse, total_q, num_qo_heads, num_splits};
     if ((st = hip_status(sinkattn::launch_merge(m, s), "merge launch")) != SINKATTN_OK) return st;
@@ -591,13 +591,13 @@ int32_t sinkattn_pick_num_splits_multi(const int32_t* kv_len_host, int32_t batch
   int64_t max_len = 0;
   for (int32_t b = 0; b < batch; ++b) max_len = kv_len_host[b] > max_len ? kv_len_host[b] : max_len;
   const int64_t max_pages = (max_len + SINKATTN_PAGE_SIZE - 1) / SINKATTN_PAGE_SIZE;
-  // The several-row kernel holds one workgroup per CU for each wave it keeps
-  // per SIMD: 6, 4 or 3 for one, two or four 16-column blocks.  Aim for about
-  // 4/3 of the resident workgroups (twice with a mask, whose pages cost more)
-  // so that one round plus a short tail covers the batch: fewer, longer
-  // chunks than the one-row rule, which measured best on the verify batch.
-  const int64_t cols = (int64_t)(num_qo_heads / num_kv_heads) * max_qo_len;
-  const int64_t per_cu = cols <= 16 ? 6 : cols <= 32 ? 4 : 3;
+  // The several-row kernel runs two workgroups per CU (two waves per SIMD).
+  // Aim for about 4/3 of the resident workgroups (twice with a mask, whose
+  // pages cost more) so that one round plus a short tail covers the batch:
+  // fewer, longer chunks than the one-row rule; on the verify batch (512
+  // (request, KV head) units) this gives two chunks, which measured best
+  // with and without masks (69.5 / 96.2 us against 74.7 / 101.6 at three).
+  const int64_t per_cu = 2;
   const int64_t target = 256 * per_cu * (with_mask ? 2 : 4) / (with_mask ? 1 : 3);
   const int64_t units = (int64_t)batch * num_kv_heads;
   int64_t s = (target + units - 1) / units;

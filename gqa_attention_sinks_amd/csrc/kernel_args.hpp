@@ -109,6 +109,7 @@ struct MoeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_verify(const DecodeArgs& a, hipStream_t stream);   // several rows per request
 hipError_t launch_decode_balanced(const BalancedArgs& a, hipStream_t stream);   // pieces
 hipError_t launch_merge_balanced(const BalancedArgs& a, hipStream_t stream);
 hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream);

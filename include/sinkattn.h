@@ -401,11 +401,11 @@ sinkattn_status sinkattn_split_bounds(const int32_t* kv_len_host, int32_t batch,
 int32_t sinkattn_pick_num_splits(const int32_t* kv_len_host, int32_t batch, int32_t num_kv_heads);
 
 /* Host-only: a split count for sinkattn_decode_paged_multi (kv_len_host
- * [batch], host; max_qo_len and with_mask as in the call).  That kernel keeps
- * fewer waves per SIMD the more (row, head) columns a KV head has, so it is
- * given fewer, longer chunks than the one-row rule gives: about 4/3 of the
- * workgroups the GPU holds at once (twice that with a mask), chunks of at
- * least 16 pages, at most 16 of them.  Returns 1 on invalid arguments. */
+ * [batch], host; max_qo_len and with_mask as in the call).  That kernel runs
+ * two workgroups per compute unit, so it is given fewer, longer chunks than
+ * the one-row rule gives: about 4/3 of the workgroups the GPU holds at once
+ * (twice that with a mask), chunks of at least 16 pages, at most 16 of them.
+ * Returns 1 on invalid arguments. */
 int32_t sinkattn_pick_num_splits_multi(const int32_t* kv_len_host, int32_t batch, int32_t num_qo_heads,
                                        int32_t num_kv_heads, int32_t max_qo_len, int32_t with_mask);
 

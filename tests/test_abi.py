@@ -73,11 +73,12 @@ def test_pick_num_splits_is_in_range(lib):
 
 def test_pick_num_splits_multi(lib):
     lens = np.full(64, 4096)
-    # four column blocks (8 heads x 8 rows): three workgroups per CU -> about
-    # 1024 units without a mask, 1536 with one, over 512 (request, KV head) pairs
+    # two workgroups per CU (512 at once): about 683 units without a mask and
+    # 1024 with one, over 512 (request, KV head) pairs
     assert sa.pick_num_splits_multi(lens, 64, 8, 8) == 2
-    assert sa.pick_num_splits_multi(lens, 64, 8, 8, with_mask=True) == 3
-    assert sa.pick_num_splits_multi(lens, 64, 8, 2) == 4          # one block: six per CU, 2048 units
+    assert sa.pick_num_splits_multi(lens, 64, 8, 8, with_mask=True) == 2
+    assert sa.pick_num_splits_multi(lens, 64, 8, 2) == 2          # the same kernel for any row count
+    assert sa.pick_num_splits_multi(np.full(16, 4096), 64, 8, 8) == 6
     assert sa.pick_num_splits_multi(np.full(4, 10), 64, 8, 8) == 1   # chunks of at least 16 pages
     assert sa.pick_num_splits_multi(np.full(2, 1 << 20), 64, 8, 8) == 16
     assert lib.sinkattn_pick_num_splits_multi(None, 4, 64, 8, 8, 0) == 1

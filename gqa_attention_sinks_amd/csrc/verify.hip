@@ -45,6 +45,7 @@ constexpr int kVThreads = kVW * 64;
 constexpr int kStepKeys = 2 * kPageSize;                // keys per step: two pages
 constexpr int kStageBytes = kStepKeys * kHeadDim * 2;   // a wave's V of one step, fp16: 4 KiB
 constexpr float kSumLimit = 16384.f;                    // 2^14
+constexpr int kMaxRows = 8;                             // query rows per request at most
 constexpr float kFloatMax = 3.402823466e38f;
 // s_waitcnt operand: vector memory count 0, the other counters unconstrained
 // (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
@@ -149,7 +150,39 @@ void verify_kernel(DecodeArgs a) {
     c_bit[cb] = t < n_q ? t * n_k : -1;
   }
   const uint8_t* mbytes = MASK ? a.custom_mask + a.mask_indptr[b] : nullptr;
+  // MASK: per row, the first hidden key of the chunk (t_hi when none).  The
+  // steps below it show all their keys to that row, so only the others read
+  // mask bits per lane; a draft tree shows its rows the whole context, so that
+  // is every step but the last one or two.  One pass over the chunk's bits,
+  // 32 keys per thread and word (the bytes read stop at the row's last key).
+  __shared__ int s_fz[kMaxRows];
+  int fz[2] = {0x7fffffff, 0x7fffffff};
+  if (MASK) {
+    if (tid < kMaxRows) s_fz[tid] = t_hi;
+    __syncthreads();
+    const int nw = t_hi > t_lo ? (t_hi - t_lo + 31) / 32 : 0;   // words per row
+    for (int w = tid; w < n_q * nw; w += kVThreads) {
+      const int t = w / nw;
+      const int key0 = t_lo + 32 * (w - t * nw);
+      const int n = min(32, t_hi - key0);
+      const int bit0 = t * n_k + key0;
+      const int last = (bit0 + n - 1) >> 3;
+      uint64_t x = 0;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) x |= (uint64_t)mbytes[min((bit0 >> 3) + i, last)] << (8 * i);
+      const uint32_t valid = n == 32 ? 0xFFFFFFFFu : ((1u << n) - 1u);
+      const uint32_t hidden = ~(uint32_t)(x >> (bit0 & 7)) & valid;
+      if (hidden != 0u) atomicMin(&s_fz[t], key0 + __builtin_ctz(hidden));
+    }
+  }
   __syncthreads();
+  if (MASK) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int t = (32 * cb + r32) / G;
+      if (t < n_q) fz[cb] = s_fz[t];
+    }
+  }
 
   // Key-domain state per column block: reference m (base 2; at or below the
   // key maximum seen), this lane's part of the denominator, O^T accumulator.
@@ -190,16 +223,13 @@ void verify_kernel(DecodeArgs a) {
   };
   // The step at page p: lane l reads key l % 32 (page p or p + 1; past the
   // run the last page again), 16 bytes of K and of V per k step.  Two
-  // register sets alternate between steps.  Without a mask the step after
-  // the current one is in flight while it computes (its loads go to the
-  // other set once the current step's V is staged); with a mask, whose bit
-  // loads must not wait behind page loads, the set a step has just freed is
-  // refilled with the step two ahead (measured on the verify batch: one step
-  // ahead 69.5 against 75.4 us unmasked, two ahead 96.2 against 100.5 us
-  // masked).  Every path issues the same loads (a step past the run reloads
-  // the run's last pages, a cache hit): the compiler's count of loads in
-  // flight then stays exact, and a step waits for its own pages only.
-  constexpr int LA = MASK ? 2 : 1;                       // steps of lookahead
+  // register sets alternate between steps: the next step's pages go to the
+  // other set once the current step's V is staged, so they are in flight
+  // while it computes (two steps ahead, refilling the set a step frees,
+  // measured slower: 75.4 against 69.5 us on the verify batch).  Every path
+  // issues the same loads (a step past the run reloads the run's last pages,
+  // a cache hit): the compiler's count of loads in flight then stays exact,
+  // and a step waits for its own pages only.
   const int n_steps = (wp1 - wp0 + 1) / 2;
   const int p_last = wp0 + 2 * max(n_steps - 1, 0);    // the run's last step
   u32x4 kA[4], vA[4], kB[4], vB[4];
@@ -216,10 +246,7 @@ void verify_kernel(DecodeArgs a) {
     }
   };
 
-  if (n_steps > 0) {
-    load_step(wp0, kA, vA);
-    if (LA == 2) load_step(wp0 + 2, kB, vB);
-  }
+  if (n_steps > 0) load_step(wp0, kA, vA);
   // step st with its pages in (kc, vc); (kn, vn): the other set
   auto step = [&](const int st, u32x4 (&kc)[4], u32x4 (&vc)[4], u32x4 (&kn)[4], u32x4 (&vn)[4])
       __attribute__((always_inline)) {
@@ -250,23 +277,9 @@ void verify_kernel(DecodeArgs a) {
       }
     }
     __asm__ volatile("" ::: "memory");
-    // MASK: the step's mask bits, loaded before the prefetch below so that
-    // waiting for them does not wait for it
-    uint32_t mb[2] = {0xFFFFu, 0xFFFFu};   // MASK: bit i = element i of the lane's scores
-    if (MASK) {
-#pragma unroll
-      for (int cb = 0; cb < 2; ++cb) {
-        if (cb >= nb_used || c_bit[cb] < 0) { mb[cb] = 0u; continue; }
-        uint32_t w = 0;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) w |= mask4(mbytes, c_bit[cb], key_base + 8 * q4 + 4 * half, n_k) << (4 * q4);
-        mb[cb] = w;
-      }
-    }
-    // the pages LA steps ahead
-    advance_ids(min(p + 2 * LA, p_last));
-    if (LA == 2) load_step(p + 4, kc, vc);
-    else load_step(p + 2, kn, vn);
+    // the next step's pages
+    advance_ids(min(p + 2, p_last));
+    load_step(p + 2, kn, vn);
 
     // visibility: the common step shows every key to every real column
     const bool step_in = key_base >= t_lo && key_base + kStepKeys <= run_end;
@@ -274,14 +287,22 @@ void verify_kernel(DecodeArgs a) {
     for (int cb = 0; cb < 2; ++cb) {
       if (cb >= nb_used) continue;
       bool full;
-      if (MASK) full = step_in && __builtin_amdgcn_ballot_w64(c_bit[cb] >= 0 && mb[cb] != 0xFFFFu) == 0;
+      if (MASK) full = step_in && __builtin_amdgcn_ballot_w64(c_bit[cb] >= 0 && key_base + kStepKeys > fz[cb]) == 0;
       else full = step_in && key_base >= full_lo && key_base + kStepKeys - 1 <= full_hi;
       if (!full) {   // uniform: the chunk's edges, the diagonal, the window edge, masks with holes
+        uint32_t mb = 0xFFFFu;   // MASK: bit i = element i of the lane's scores
+        if (MASK) {
+          mb = 0u;
+          if (c_bit[cb] >= 0) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) mb |= mask4(mbytes, c_bit[cb], key_base + 8 * q4 + 4 * half, n_k) << (4 * q4);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = key_base + 8 * (i >> 2) + 4 * half + (i & 3);
           bool vis = key >= v_lo[cb] && key <= v_hi[cb] && key < run_end;
-          if (MASK) vis = vis && ((mb[cb] >> i) & 1u);
+          if (MASK) vis = vis && ((mb >> i) & 1u);
           s[cb][i] = vis ? s[cb][i] : kNegInf;
         }
       }

@@ -118,6 +118,8 @@ def sub_batch(w, reqs):
     rows = np.concatenate([np.arange(qo[b], qo[b + 1]) for b in reqs]) if len(reqs) else np.zeros(0, np.int64)
     qo_len = qo[reqs + 1] - qo[reqs]
     new = wl.Workload(**{**w.__dict__})
+    if "masks" in w.meta:
+        new.meta = {**w.meta, "masks": [w.meta["masks"][b] for b in reqs]}
     new.q = w.q[rows]
     new.qo_indptr = np.concatenate([[0], np.cumsum(qo_len)]).astype(np.int32)
     new.kv_len = np.asarray(w.kv_len)[reqs].astype(np.int32)
@@ -201,7 +203,8 @@ def _oracle_job(key):
         o_part, lse_part = oracle.split_partials_ref(w.q, kv, w.sinks, w.scale, w.num_splits, window, workers=1)
         out, lse = oracle.merge_ref(o_part, lse_part)
     else:
-        out, lse = oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, window, workers=1)
+        out, lse = oracle.sink_attention_ref(w.q, w.qo_indptr, kv, w.sinks, w.scale, window, workers=1,
+                                             custom_mask=w.meta.get("masks"))
     return key, out.astype(np.float32), lse.astype(np.float32), time.perf_counter() - t0
 
 
@@ -286,6 +289,16 @@ def run_oracles(ws, cores):
     jobs = [(sub_batch(w, g), 0, "attn", np.asarray(g)) for g in groups]
     oc.run("skewed_decode", jobs, decode_bytes(w), "GB/s",
            f"whole workload ({w.batch} requests, {int(w.kv_len.sum())} keys) in {len(groups)} sub-batches")
+    # verify (several rows per request), with and without draft-tree masks:
+    # the whole batch in balanced sub-batches
+    for name in ("verify_decode", "verify_tree"):
+        if name not in ws:
+            continue
+        w = ws[name]
+        groups = balanced_groups(np.asarray(w.kv_len) * np.diff(w.qo_indptr), cores)
+        jobs = [(sub_batch(w, g), 0, "attn", np.asarray(g)) for g in groups]
+        oc.run(name, jobs, decode_bytes(w), "GB/s",
+               f"whole workload ({w.batch} requests, {int(w.qo_indptr[-1])} rows) in {len(groups)} sub-batches")
     # mixed batch, 128-key window: the whole call
     w = ws["mixed_batch"]
     n_pre = int(w.meta["n_prefill"])
@@ -597,6 +610,13 @@ DESCR = {
     "mixed_batch": "mixed batch: 16 prefill chunks of 512 tokens on prefixes uniform in [0, 16384] + 240 decode "
                    "rows with KV lengths uniform in [1, 16384] in one call, 64 query / 8 KV heads, paged "
                    "(page 16), sinks N(0, 2), seed 0",
+    "verify_decode": "verify decode (NEXT row): batch 64, KV lengths uniform in [8, 4096], query rows per request "
+                     "uniform in [2, 8], 64 query / 8 KV heads, paged (page 16), sinks N(0, 2), seed 0",
+    "verify_tree": "draft-tree verify (NEXT row): the verify batch with a random draft tree (custom mask) per "
+                   "request, seed 0",
+    "append_rope": "paged KV append with rotary embedding (NEXT row): 16 chunks of 512 new tokens on prefixes "
+                   "uniform in [0, 16384], 64 query / 8 KV heads, random pages, seed 0",
+    "moe_topk": "MoE routing weights (NEXT row): 65536 tokens x 128 experts of bf16 logits N(0, 1), top 4, seed 0",
 }
 
 
@@ -716,6 +736,31 @@ def leg_mixed(w, window, args, torch, dev, oc):
             "cpu_baseline": oc.baselines.get(name) if oc else None}
 
 
+def leg_verify(name, w, args, torch, dev, oc):
+    """Several query rows per request (sinkattn_decode_paged_multi), with or
+    without draft-tree masks: the decode kernel per launch (replicas
+    rotated), the whole call (decode + merge) by wall clock, parity of one
+    whole call against the oracle."""
+    res = time_verify(w, args, torch, dev)
+    nbytes = decode_bytes(w)
+    return {"workload": DESCR[name], "bound": "hbm", "num_splits": res["splits"],
+            "rows": int(w.qo_indptr[-1]), "step_ms_wall": round(res["step_ms"], 5),
+            "kernels": {"verify_kernel": {"ms": res["decode"], "algorithmic_bytes": nbytes,
+                                          "roofline": roofline_entry("verify_kernel", "hbm", nbytes,
+                                                                     res["decode"]["mean"])}},
+            "parity": parity_from_oracle(oc, name, w, res["out"], res["lse"]),
+            "cpu_baseline": oc.baselines.get(name) if oc else None}
+
+
+def leg_bytes(name, r):
+    """A bandwidth-bound NEXT-row kernel timed by graph replay (its parity
+    against the oracle is covered by the GPU tests)."""
+    return {"workload": DESCR[name], "bound": "hbm", "ms_per_call_graph": round(r["ms"], 5),
+            "kernels": {name: {"ms": {"mean": round(r["ms"], 5)}, "algorithmic_bytes": r["bytes"],
+                               "roofline": roofline_entry(name, "hbm", r["bytes"], r["ms"])}},
+            "parity": None}
+
+
 # ---------------------------------------------------------------------------
 # main
 # ---------------------------------------------------------------------------
@@ -732,7 +777,7 @@ def main():
     t_start = time.perf_counter()
     log("generating workloads")
     ws = {n: getattr(wl, n)() for n in ["tiny_prefill", "paged_decode", "causal_prefill", "long_split_decode",
-                                         "mixed_batch", "skewed_decode"]}
+                                         "mixed_batch", "skewed_decode", "verify_decode", "verify_tree"]}
     cores = len(os.sched_getaffinity(0))
     oc = None
     if not args.no_cpu:
@@ -772,6 +817,13 @@ def main():
                                                       "balanced")
     configs["skewed_decode_split"], _ = leg_decode("skewed_decode", ws["skewed_decode"], args, torch, dev, oc,
                                                    "split")
+    torch.cuda.empty_cache()
+    for name in ("verify_decode", "verify_tree"):
+        log(name)
+        configs[name] = leg_verify(name, ws[name], args, torch, dev, oc)
+    log("append_rope, moe_topk")
+    configs["append_rope"] = leg_bytes("append_rope", time_append(args, torch, dev))
+    configs["moe_topk"] = leg_bytes("moe_topk", time_moe(args, torch, dev))
     torch.cuda.empty_cache()
     for window in (128, 0):
         log(f"mixed_batch window={window}")
@@ -892,7 +944,18 @@ def time_verify(w, args, torch, dev):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
     dec = launch_times(lambda i: call(i, False), max(args.steps, 100), stream, torch)
-    return dict(step_ms=wall * 1e3, decode=stats_ms(dec), splits=s)
+    # one whole call (decode + merge) on replica 0 with its LSE, for parity
+    r0 = reps[0]
+    out0 = torch.empty_like(r0.q)
+    lse0 = torch.empty((TQ, H), dtype=torch.float32, device=dev)
+    st = lib.sinkattn_decode_paged_multi(P(r0.q.data_ptr()), P(r0.qo_indptr.data_ptr()), mask, mask_ptr,
+                                         ctypes.byref(kvs[0]), P(r0.sinks.data_ptr()), s, P(out0.data_ptr()),
+                                         opart if s > 1 else None, lpart if s > 1 else None, P(lse0.data_ptr()),
+                                         B, TQ, R, H, HKV, 64, scale, 0, sp)
+    if st != 0:
+        raise RuntimeError(lib.sinkattn_last_error().decode())
+    torch.cuda.synchronize()
+    return dict(step_ms=wall * 1e3, decode=stats_ms(dec), splits=s, out=to_host(out0), lse=to_host(lse0))
 
 
 def time_append(args, torch, dev):

@@ -573,20 +573,34 @@ def graph_call_ms(call, n, torch):
     return e0.elapsed_time(e1) / n
 
 
-def measured_traffic(kernel, workload, splits):
-    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE runs, or
-    None when the kernel's sources changed since they were taken."""
+# The sources each kernel is built from: a traffic record (HBM bytes per
+# launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs) holds their hash and is
+# used only while it matches.
+KERNEL_SOURCES = {
+    "decode_paged_kernel": ("decode.hip", "decode_common.hpp"),
+    "decode_balanced_kernel": ("decode_balanced.hip",),
+    "prefill_kernel": ("prefill.hip", "mfma_tile.hpp"),
+    "verify_kernel": ("verify.hip", "decode_common.hpp", "mfma_tile.hpp"),
+}
+
+
+def kernel_source_hash(kernel):
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path)).get(kernel)
     csrc = os.path.join(ROOT, "gqa_attention_sinks_amd", "csrc")
-    srcs = (("decode_balanced.hip",) if kernel == "decode_balanced_kernel" else ("decode.hip", "decode_common.hpp"))
-    files = [os.path.join(csrc, f) for f in (*srcs, "device_common.hpp", "kernel_args.hpp")]
-    digest = hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
-    if not rec or rec.get("source_sha256") != digest or rec.get("workload") != workload \
-            or rec.get("num_splits") != splits:
+    files = [os.path.join(csrc, f) for f in (*KERNEL_SOURCES[kernel], "device_common.hpp", "kernel_args.hpp")]
+    return hashlib.sha256(b"".join(open(f, "rb").read() for f in files)).hexdigest()
+
+
+def measured_traffic(kernel, workload, splits=None):
+    """HBM bytes per launch of ``kernel`` on ``workload`` from the committed
+    FETCH_SIZE/WRITE_SIZE runs (profiles/traffic.json), or None when there is
+    no record or the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path) or kernel not in KERNEL_SOURCES:
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_sha256") != kernel_source_hash(kernel) or \
+            (splits is not None and rec.get("num_splits") != splits):
         return None
     return int(round(rec["bytes"]))
 
@@ -632,7 +646,8 @@ def leg_tiny(w, args, torch, dev, oc):
     st = stats_ms(r["times"])
     return {"workload": DESCR["tiny_prefill"], "bound": "latency (launch)",
             "kernels": {"prefill_kernel": {"ms": st, "algorithmic_flops": flops,
-                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"])}},
+                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"],
+                                                                      measured_traffic("prefill_kernel", "tiny_prefill"))}},
             "call_ms_graph_replay": round(graph_ms, 5),
             "parity": parity_from_oracle(oc, "tiny_prefill", w, r["out"], r["lse"]),
             "cpu_baseline": oc.baselines.get("tiny_prefill") if oc else None}
@@ -644,7 +659,8 @@ def leg_causal_prefill(w, args, torch, dev, oc):
     st = stats_ms(r["times"])
     return {"workload": DESCR["causal_prefill"], "bound": "mfma",
             "kernels": {"prefill_kernel": {"ms": st, "algorithmic_flops": flops,
-                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"])}},
+                                           "roofline": roofline_entry("prefill_kernel", "mfma", flops, st["mean"],
+                                                                      measured_traffic("prefill_kernel", "causal_prefill"))}},
             "parity": parity_from_oracle(oc, "causal_prefill", w, r["out"], r["lse"]),
             "cpu_baseline": oc.baselines.get("causal_prefill") if oc else None}
 
@@ -655,7 +671,8 @@ def leg_decode(name, w, args, torch, dev, oc, mode):
     dst, mst = stats_ms(res["decode"]), stats_ms(res["merge"])
     kname = "decode_balanced_kernel" if mode == "balanced" else "decode_paged_kernel"
     kernels = {kname: {"ms": dst, "algorithmic_bytes": nbytes,
-                       "roofline": roofline_entry(kname, "hbm", nbytes, dst["mean"])}}
+                       "roofline": roofline_entry(kname, "hbm", nbytes, dst["mean"],
+                                                  measured_traffic(kname, name, res["splits"]))}}
     if mode == "balanced":
         kernels["merge_balanced_kernel"] = {"ms": mst}
     elif res["splits"] > 1:
@@ -727,10 +744,12 @@ def leg_mixed(w, window, args, torch, dev, oc):
             "call_frac_of_sum_bound": round(bound_ms / wst["mean"], 4),
             "kernels": {
                 "prefill_kernel": {"ms": pst, "algorithmic_flops": flops, "rows": d0,
-                                   "roofline": roofline_entry("prefill_kernel", "mfma", flops, pst["mean"])},
+                                   "roofline": roofline_entry("prefill_kernel", "mfma", flops, pst["mean"],
+                                                              measured_traffic("prefill_kernel", name))},
                 "decode_paged_kernel": {"ms": dst, "algorithmic_bytes": nbytes, "rows": nd,
                                         "roofline": roofline_entry("decode_paged_kernel", "hbm", nbytes,
-                                                                   dst["mean"])}},
+                                                                   dst["mean"],
+                                                                   measured_traffic("decode_paged_kernel", name))}},
             "decode_rows_alone_equal_whole_call": same,
             "parity": parity_from_oracle(oc, name, w, whole["out"], whole["lse"]),
             "cpu_baseline": oc.baselines.get(name) if oc else None}
@@ -747,7 +766,9 @@ def leg_verify(name, w, args, torch, dev, oc):
             "rows": int(w.qo_indptr[-1]), "step_ms_wall": round(res["step_ms"], 5),
             "kernels": {"verify_kernel": {"ms": res["decode"], "algorithmic_bytes": nbytes,
                                           "roofline": roofline_entry("verify_kernel", "hbm", nbytes,
-                                                                     res["decode"]["mean"])}},
+                                                                     res["decode"]["mean"],
+                                                                     measured_traffic("verify_kernel", name,
+                                                                                      res["splits"]))}},
             "parity": parity_from_oracle(oc, name, w, res["out"], res["lse"]),
             "cpu_baseline": oc.baselines.get(name) if oc else None}
 

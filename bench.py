@@ -68,6 +68,8 @@ def parse():
     p.add_argument("--decode", default="split", choices=["balanced", "split"],
                    help="the decode path of the headline (the other is timed beside it)")
     p.add_argument("--replicas", type=int, default=3)
+    p.add_argument("--no-host-order", action="store_true",
+                   help="paged decode calls without the host copy of kv_len (the kernels rank the batch)")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle (no cpu_baseline, no parity)")
     p.add_argument("--workload", default=None, choices=WORKLOADS,
                    help="for profiling runs: time only this workload (copy_calibration: a plain 256 MiB "
@@ -441,7 +443,8 @@ def time_decode(w, args, torch, dev, window=0, mode="balanced"):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = ctypes.c_void_p
-    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len) for r in reps]
+    host_len = None if args.no_host_order else w.kv_len
+    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len, host_len) for r in reps]
     qp = [P(r.q.data_ptr()) for r in reps]
     sk = [P(r.sinks.data_ptr()) for r in reps]
     op = [P(o.data_ptr()) for o in outs]
@@ -533,7 +536,7 @@ def time_decode(w, args, torch, dev, window=0, mode="balanced"):
                 out=out_host, lse=lse_host)
 
 
-def time_prefill(w, n, warmup, torch, dev, window=0, d=None, group=10):
+def time_prefill(w, n, warmup, torch, dev, window=0, d=None, group=10, host_order=True):
     """sinkattn_prefill on a workload, each call between events; returns the
     per-call times and the output."""
     from gqa_attention_sinks_amd import binding
@@ -546,7 +549,7 @@ def time_prefill(w, n, warmup, torch, dev, window=0, d=None, group=10):
     def call(i=0):
         binding.prefill(d.q, d.qo_indptr, d.k, d.v, d.kv_indptr, d.sinks, w.scale, window=window,
                         page_indices=d.page_indices, kv_len=d.kv_len if w.paged else None, out=out, lse=lse,
-                        qo_indptr_host=host)
+                        qo_indptr_host=host, kv_len_host=w.kv_len if (w.paged and host_order) else None)
 
     for _ in range(warmup):
         call()
@@ -700,7 +703,8 @@ def leg_mixed(w, window, args, torch, dev, oc):
     n_pre = int(w.meta["n_prefill"])
     d = Dev(w, torch, dev)
     n, group = (40, 2) if window == 0 else (200, 10)
-    whole = time_prefill(w, n, 3, torch, dev, window=window, d=d, group=group)
+    ho = not args.no_host_order
+    whole = time_prefill(w, n, 3, torch, dev, window=window, d=d, group=group, host_order=ho)
     pre_w = sub_batch(w, range(n_pre))
     dp = Dev.__new__(Dev)
     dp.__dict__ = dict(d.__dict__)
@@ -708,13 +712,14 @@ def leg_mixed(w, window, args, torch, dev, oc):
     dp.qo_indptr = d.qo_indptr[:n_pre + 1]
     dp.kv_indptr = d.kv_indptr[:n_pre + 1]
     dp.kv_len = d.kv_len[:n_pre]
-    pre = time_prefill(pre_w, n, 3, torch, dev, window=window, d=dp, group=group)
+    pre = time_prefill(pre_w, n, 3, torch, dev, window=window, d=dp, group=group, host_order=ho)
     # decode rows: request b >= n_pre owns row qo_indptr[b] = d0 + (b - n_pre)
     d0 = int(w.qo_indptr[n_pre])
     dec_w = sub_batch(w, range(n_pre, w.batch))
     q_dec = d.q[d0:]
     out_dec = torch.empty_like(q_dec)
-    kv = binding.kv_descriptor(d.k, d.v, d.kv_indptr[n_pre:], d.page_indices, d.kv_len[n_pre:])
+    kv = binding.kv_descriptor(d.k, d.v, d.kv_indptr[n_pre:], d.page_indices, d.kv_len[n_pre:],
+                               w.kv_len[n_pre:] if ho else None)
     lib = sa.load_library()
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -878,6 +883,8 @@ def main():
             "workload": DESCR["paged_decode"],
             "decode_path": args.decode,
             ("num_segments" if args.decode == "balanced" else "num_splits"): res["splits"],
+            "work_order": "longest request first, "
+                          + ("ranked by the kernel" if args.no_host_order else "ordered on the host"),
             "kv_replicas_rotated": args.replicas,
             "algorithmic_bytes": nbytes,
             "compute": "bf16 Q.K^T and fp16 P.V on MFMA, fp32 accumulation",
@@ -935,7 +942,8 @@ def time_verify(w, args, torch, dev):
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
     P = ctypes.c_void_p
-    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len) for r in reps]
+    host_len = None if args.no_host_order else w.kv_len
+    kvs = [binding.kv_descriptor(r.k, r.v, r.kv_indptr, r.page_indices, r.kv_len, host_len) for r in reps]
     scale = ctypes.c_float(w.scale)
     opart, lpart = P(o_part.data_ptr()), P(lse_part.data_ptr())
     mask = mask_ptr = None

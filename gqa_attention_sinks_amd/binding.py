@@ -68,6 +68,7 @@ class _KV(ctypes.Structure):
         ("page_indices", ctypes.c_void_p),
         ("kv_len", ctypes.c_void_p),
         ("num_pages", ctypes.c_int64),
+        ("kv_len_host", ctypes.c_void_p),
     ]
 
 
@@ -182,7 +183,7 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
+def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None, kv_len_host=None):
     torch = _torch()
     paged = page_indices is not None
     _dev(k, "k", torch.bfloat16)
@@ -197,9 +198,16 @@ def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
         _dev(kv_len, "kv_len", torch.int32)
     elif k.dim() != 3 or k.shape[2] != HEAD_DIM:
         raise ValueError("contiguous k/v must be [total_kv, Hkv, 64]")
-    return _KV(k.data_ptr(), v.data_ptr(), int(paged), PAGE_SIZE, kv_indptr.data_ptr(),
-               page_indices.data_ptr() if paged else None, kv_len.data_ptr() if paged else None,
-               int(k.shape[0]))
+    host = None
+    if kv_len_host is not None:
+        host = np.ascontiguousarray(kv_len_host, dtype=np.int32)
+        if host.shape != (kv_indptr.numel() - 1,):
+            raise ValueError("kv_len_host must have one entry per request")
+    kvs = _KV(k.data_ptr(), v.data_ptr(), int(paged), PAGE_SIZE, kv_indptr.data_ptr(),
+              page_indices.data_ptr() if paged else None, kv_len.data_ptr() if paged else None,
+              int(k.shape[0]), None if host is None else host.ctypes.data)
+    kvs._kv_len_host = host   # the struct points into it
+    return kvs
 
 
 # --------------------------------------------------------------------------
@@ -208,7 +216,7 @@ def _kv_struct(k, v, kv_indptr, page_indices=None, kv_len=None):
 
 def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int = 0,
             page_indices=None, kv_len=None, out=None, lse=None, return_lse: bool = False,
-            qo_indptr_host=None, stream=None):
+            qo_indptr_host=None, kv_len_host=None, stream=None):
     """Causal / sliding-window prefill (``sinkattn_prefill``).
 
     ``q`` [total_q, Hq, 64] bf16; ``qo_indptr`` [B+1] int32.  Contiguous KV:
@@ -216,7 +224,9 @@ def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int =
     ``k``/``v`` [num_pages, Hkv, 16, 64] with ``kv_indptr`` page offsets,
     ``page_indices`` and ``kv_len``.  ``sinks`` [Hq] fp32 or None.
     ``qo_indptr_host``: optional host copy of ``qo_indptr`` (numpy/list) that
-    lets the library size the launch exactly.
+    lets the library size the launch exactly.  ``kv_len_host``: optional host
+    copy of ``kv_len`` (paged) that orders the one-row requests' work on the
+    host; it never changes the results.
     Returns ``out`` (and ``lse`` [total_q, Hq] fp32 when asked).
     """
     torch = _torch()
@@ -226,7 +236,7 @@ def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int =
     total_q, hq, _ = q.shape
     _dev(qo_indptr, "qo_indptr", torch.int32)
     batch = qo_indptr.numel() - 1
-    kvs = _kv_struct(k, v, kv_indptr, page_indices, kv_len)
+    kvs = _kv_struct(k, v, kv_indptr, page_indices, kv_len, kv_len_host)
     hkv = k.shape[1]
     if sinks is not None:
         _dev(sinks, "sinks", torch.float32, (hq,))
@@ -253,20 +263,24 @@ def prefill(q, qo_indptr, k, v, kv_indptr, sinks, sm_scale: float, window: int =
 
 def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm_scale: float,
                  num_splits: int = 1, window: int = 0, out=None, o_part=None, lse_part=None,
-                 lse=None, return_lse: bool = False, merge: bool = True, stream=None):
+                 lse=None, return_lse: bool = False, merge: bool = True, kv_len_host=None,
+                 stream=None):
     """One query token per request over a paged cache (``sinkattn_decode_paged``).
 
     With ``num_splits`` > 1 the per-chunk partials ``o_part`` [B, Hq, S, 64]
     and ``lse_part`` [B, Hq, S] (allocated if not given) are written; with
     ``merge`` they are also merged into ``out`` in the same call.  Returns
     ``out`` (and ``lse``), or ``(o_part, lse_part)`` when ``merge`` is False.
+    ``kv_len_host``: optional host copy of ``kv_len`` with which the library
+    orders the work units (longest request first) on the host instead of in
+    every workgroup; it never changes the results.
     """
     torch = _torch()
     _dev(q, "q", torch.bfloat16)
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be [batch, Hq, 64]")
     batch, hq, _ = q.shape
-    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len, kv_len_host)
     hkv = k_pool.shape[1]
     if sinks is not None:
         _dev(sinks, "sinks", torch.float32, (hq,))
@@ -301,7 +315,7 @@ def decode_paged(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm
 
 def decode_paged_noalloc(q, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks, sm_scale: float,
                          num_splits: int = 1, window: int = 0, out=None, lse=None, return_lse: bool = False,
-                         stream=None):
+                         kv_len_host=None, stream=None):
     """``sinkattn_decode_paged_noalloc``: like :func:`decode_paged` with the
     merge, the split partials in the library's own device array (nothing is
     allocated by the library; ``out`` and ``lse`` are allocated here when not
@@ -311,7 +325,7 @@ def decode_paged_noalloc(q, k_pool, v_pool, page_indptr, page_indices, kv_len, s
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
         raise ValueError("q must be [batch, Hq, 64]")
     batch, hq, _ = q.shape
-    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len, kv_len_host)
     if sinks is not None:
         _dev(sinks, "sinks", torch.float32, (hq,))
     if out is None:
@@ -409,14 +423,16 @@ def balanced_workspace_segments(workspace, batch: int):
 def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, kv_len, sinks,
                        sm_scale: float, max_qo_len: int, num_splits: int = 1, window: int = 0,
                        out=None, o_part=None, lse_part=None, lse=None, return_lse: bool = False,
-                       merge: bool = True, custom_mask=None, mask_indptr=None, stream=None):
+                       merge: bool = True, custom_mask=None, mask_indptr=None, kv_len_host=None,
+                       stream=None):
     """Several query rows per request over a paged cache
     (``sinkattn_decode_paged_multi``); ``q`` is [total_q, Hq, 64] and
     ``qo_indptr`` [B+1] int32 with 1 .. ``max_qo_len`` rows per request.
     ``custom_mask`` (uint8 bit-packed, with int32 byte offsets
     ``mask_indptr`` [B+1]) replaces the causal rule.  Partials are per query
     row: ``o_part`` [total_q, Hq, S, 64], ``lse_part``
-    [total_q, Hq, S].  Returns like :func:`decode_paged`."""
+    [total_q, Hq, S].  ``kv_len_host`` as in :func:`decode_paged`.  Returns
+    like :func:`decode_paged`."""
     torch = _torch()
     _dev(q, "q", torch.bfloat16)
     if q.dim() != 3 or q.shape[2] != HEAD_DIM:
@@ -427,7 +443,7 @@ def decode_paged_multi(q, qo_indptr, k_pool, v_pool, page_indptr, page_indices, 
     if custom_mask is not None:
         _dev(custom_mask, "custom_mask", torch.uint8)
         _dev(mask_indptr, "mask_indptr", torch.int32, (batch + 1,))
-    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len)
+    kvs = _kv_struct(k_pool, v_pool, page_indptr, page_indices, kv_len, kv_len_host)
     hkv = k_pool.shape[1]
     if sinks is not None:
         _dev(sinks, "sinks", torch.float32, (hq,))
@@ -585,7 +601,7 @@ def validate_kv_host(kv_indptr, num_pages: int, page_indices=None, kv_len=None):
         raise ValueError("kv_len must have one entry per request")
     if paged and not (0 <= int(indptr[-1]) <= pages.size):
         raise ValueError("page_indices must hold kv_indptr[-1] entries")
-    kv = _KV(None, None, int(paged), PAGE_SIZE, None, None, None, int(num_pages))
+    kv = _KV(None, None, int(paged), PAGE_SIZE, None, None, None, int(num_pages), None)
     vp = ctypes.c_void_p
     _check(load_library().sinkattn_validate_kv_host(ctypes.byref(kv), indptr.ctypes.data_as(vp),
                                                     pages.ctypes.data_as(vp) if paged else None,
@@ -598,6 +614,7 @@ def raw_library():
     return load_library()
 
 
-def kv_descriptor(k, v, kv_indptr, page_indices=None, kv_len=None) -> _KV:
-    """Build the ``sinkattn_kv`` struct for direct C-ABI calls."""
-    return _kv_struct(k, v, kv_indptr, page_indices, kv_len)
+def kv_descriptor(k, v, kv_indptr, page_indices=None, kv_len=None, kv_len_host=None) -> _KV:
+    """Build the ``sinkattn_kv`` struct for direct C-ABI calls (it keeps the
+    int32 copy of ``kv_len_host`` it points to alive)."""
+    return _kv_struct(k, v, kv_indptr, page_indices, kv_len, kv_len_host)

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 
@@ -99,6 +100,23 @@ sinkattn_status scratch_on_current_device(void** ptr) {
   return SINKATTN_OK;
 }
 
+// The longest-first order of a decode launch's requests (ties by index: the
+// order the kernels' own ranking gives), from the caller's host copy of
+// kv_len, under the same conditions as that ranking; otherwise the kernels
+// rank the batch (or take the requests in order) themselves.  Any order gives
+// the same results, so a stale or wrong host copy only costs time.
+void plan_decode_order(const sinkattn_kv* kv, int32_t batch, int32_t window, sinkattn::DecodeArgs* d) {
+  if (kv->kv_len_host == nullptr || batch < 2 || batch > sinkattn::kPlanMaxBatch ||
+      (window > 0 && window <= sinkattn::kPlanMinWindow))
+    return;
+  const int32_t* len = kv->kv_len_host;
+  int32_t idx[sinkattn::kPlanMaxBatch];
+  for (int32_t b = 0; b < batch; ++b) idx[b] = b;
+  std::stable_sort(idx, idx + batch, [len](int32_t x, int32_t y) { return len[x] > len[y]; });
+  for (int32_t r = 0; r < batch; ++r) d->order[r] = static_cast<uint16_t>(idx[r]);
+  d->planned = 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -179,6 +197,7 @@ sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const 
     d.group = a.group;
     d.num_splits = 1;
     d.window = window;
+    plan_decode_order(kv, batch, window, &d);
     if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
   }
   return SINKATTN_OK;
@@ -223,6 +242,7 @@ sinkattn_status sinkattn_decode_paged(const void* q, const sinkattn_kv* kv, cons
   d.num_splits = num_splits;
   d.window = window;
   REQUIRE((long)batch * num_kv_heads * num_splits < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
+  plan_decode_order(kv, batch, window, &d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = hip_status(sinkattn::launch_decode(d, s), "decode launch")) != SINKATTN_OK) return st;
   if (num_splits > 1 && out != nullptr) {
@@ -461,6 +481,7 @@ sinkattn_status sinkattn_decode_paged_multi(const void* q, const int32_t* qo_ind
   d.num_splits = num_splits;
   d.window = window;
   d.max_rows = max_qo_len;
+  plan_decode_order(kv, batch, window, &d);
   hipStream_t s = static_cast<hipStream_t>(stream);
   if ((st = hip_status(sinkattn::launch_decode_verify(d, s), "verify decode launch")) != SINKATTN_OK) return st;
   if (num_splits > 1 && out != nullptr) {

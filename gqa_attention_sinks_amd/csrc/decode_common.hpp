@@ -9,12 +9,13 @@ namespace sinkattn {
 
 // Requests ranked by KV length (longest first), so that the longest chunks
 // start first and the short ones fill the tail; only for batches up to this
-// size (every workgroup ranks the batch itself).  Padding entries of -1 never
-// outrank a real request (kv_len >= 0).
-constexpr int kRankMaxBatch = 256;
+// size (the host passes the order with the launch, or every workgroup ranks
+// the batch itself).  Padding entries of -1 never outrank a real request
+// (kv_len >= 0).
+constexpr int kRankMaxBatch = kPlanMaxBatch;
 // Under a window up to this long every request's work is about the same, and
 // ranking would only cost time.
-constexpr int kRankMinWindow = 2048;
+constexpr int kRankMinWindow = kPlanMinWindow;
 
 // Work unit of this workgroup: (request b, KV head g, chunk c), with the
 // request's KV length and the offset of its page list.  Units are numbered
@@ -33,6 +34,12 @@ __device__ __forceinline__ DecodeUnit decode_unit(const DecodeArgs& a) {
   unit /= a.num_kv_heads;
   u.c = unit % S;
   const int r = unit / S;
+  if (a.planned) {   // the order, built on the host (any permutation gives the same results)
+    u.b = a.order[r];
+    u.n_k = a.kv_len[u.b];
+    u.page_base = a.page_indptr[u.b];
+    return u;
+  }
   if (a.batch <= kRankMaxBatch && a.batch > 1 && (a.window == 0 || a.window > kRankMinWindow)) {
     __shared__ __attribute__((aligned(16))) int s_len[kRankMaxBatch];
     __shared__ int s_ptr[kRankMaxBatch];

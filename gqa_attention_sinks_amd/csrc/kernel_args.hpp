@@ -7,6 +7,13 @@
 
 namespace sinkattn {
 
+// Batches of 2 to this many requests run their decode work units longest
+// request first (ranked on the host when a host copy of kv_len is given, else
+// by every workgroup), unless a window of at most kPlanMinWindow keys makes
+// every request's work about the same.
+constexpr int kPlanMaxBatch = 256;
+constexpr int kPlanMinWindow = 2048;
+
 // Query rows over a paged cache, split into chunks of whole pages; see
 // sinkattn_decode_paged and sinkattn_decode_paged_multi in include/sinkattn.h.
 struct DecodeArgs {
@@ -30,6 +37,8 @@ struct DecodeArgs {
                               // outputs indexed by row
   const uint8_t* custom_mask; // optional with max_rows: bit t * n_k + j of request b's bytes
   const int32_t* mask_indptr; // (from mask_indptr[b]) = row t sees key j
+  int32_t planned;            // 1: order[] holds the requests longest first (built on the host)
+  uint16_t order[kPlanMaxBatch];
 };
 
 struct MergeArgs {

@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define SINKATTN_ABI_VERSION 7
+#define SINKATTN_ABI_VERSION 8
 #define SINKATTN_HEAD_DIM 64
 #define SINKATTN_PAGE_SIZE 16
 #define SINKATTN_MAX_SPLITS 256
@@ -114,6 +114,18 @@ typedef struct sinkattn_kv {
   const int32_t* page_indices;   /* paged only */
   const int32_t* kv_len;         /* paged only */
   int64_t num_pages;             /* capacity of k and v (pages, or rows when contiguous) */
+  /* Optional host copy of kv_len [batch] (NULL: none).  Paged decode calls
+   * (sinkattn_decode_paged, _noalloc, _multi, and the decode rows of
+   * sinkattn_prefill) run their (request, KV head, chunk) work units longest
+   * request first; with this copy the library orders them on the host and
+   * passes the order with the launch, instead of every workgroup ranking the
+   * batch's lengths ("Accelerating Sonar through speculation", section
+   * "Inference with speculative decoding": the host side of the runtime fills
+   * the buffers that configure and schedule the attention kernel for each
+   * batch).  It only orders the work: the results are
+   * the same whatever it holds (the lengths the kernels use are always the
+   * device kv_len's). */
+  const int32_t* kv_len_host;
 } sinkattn_kv;
 
 /* Causal or sliding-window prefill over a batch of requests, each with

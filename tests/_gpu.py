@@ -64,21 +64,22 @@ class DeviceWorkload:
         self.page_indices = i32_to_dev(w.page_indices) if w.paged else None
         self.sinks = f32_to_dev(w.sinks)
 
-    def prefill(self, window, sinks=True, return_lse=True, host_plan=True):
+    def prefill(self, window, sinks=True, return_lse=True, host_plan=True, kv_len_host=None):
         w = self.w
         return sa.prefill(self.q, self.qo_indptr, self.k, self.v, self.kv_indptr,
                           self.sinks if sinks else None, w.scale, window=window,
                           page_indices=self.page_indices, kv_len=self.kv_len if w.paged else None,
-                          return_lse=return_lse, qo_indptr_host=w.qo_indptr if host_plan else None)
+                          return_lse=return_lse, qo_indptr_host=w.qo_indptr if host_plan else None,
+                          kv_len_host=kv_len_host)
 
-    def decode(self, num_splits, window=0, merge=True, return_lse=True, sinks=True):
+    def decode(self, num_splits, window=0, merge=True, return_lse=True, sinks=True, kv_len_host=None):
         w = self.w
         return sa.decode_paged(self.q, self.k, self.v, self.kv_indptr, self.page_indices, self.kv_len,
                                self.sinks if sinks else None, w.scale, num_splits=num_splits, window=window,
-                               merge=merge, return_lse=return_lse)
+                               merge=merge, return_lse=return_lse, kv_len_host=kv_len_host)
 
-
-    def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True, masks=None):
+    def decode_multi(self, num_splits, max_rows, window=0, merge=True, return_lse=True, masks=None,
+                     kv_len_host=None):
         w = self.w
         mask = mask_indptr = None
         if masks is not None:
@@ -90,7 +91,8 @@ class DeviceWorkload:
         return sa.decode_paged_multi(self.q, self.qo_indptr, self.k, self.v, self.kv_indptr,
                                      self.page_indices, self.kv_len, self.sinks, w.scale, max_rows,
                                      num_splits=num_splits, window=window, merge=merge,
-                                     return_lse=return_lse, custom_mask=mask, mask_indptr=mask_indptr)
+                                     return_lse=return_lse, custom_mask=mask, mask_indptr=mask_indptr,
+                                     kv_len_host=kv_len_host)
 
 
 def kv_cache(w):

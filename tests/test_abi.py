@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version(lib):
-    assert sa.abi_version() == 7
+    assert sa.abi_version() == 8
     assert lib.sinkattn_status_string(0) == b"ok"
     assert lib.sinkattn_status_string(2) == b"unsupported"
 

@@ -15,6 +15,7 @@ spread over all host cores.
 import numpy as np
 import pytest
 
+import gqa_attention_sinks_amd as sa
 import oracle
 from gqa_attention_sinks_amd import workloads as wl
 from tests._gpu import (DeviceWorkload, assert_parity, assert_parity_by_request, host_workers, kv_cache,
@@ -274,6 +275,52 @@ def test_prefill_uneven_ranked_order_windowed():
 # merge entry point
 # ---------------------------------------------------------------------------
 
+def _host_copies(w):
+    """The right host copy of kv_len, a reversed (wrong) one and a constant one:
+    each orders the work differently, none may change a result."""
+    lens = np.asarray(w.kv_len, dtype=np.int32)
+    return {"right": lens, "reversed": lens[::-1].copy(), "constant": np.zeros_like(lens)}
+
+
+def _same(a, b, what):
+    for x, y in zip(a, b):
+        assert np.array_equal(to_host(x), to_host(y)), f"{what}: results differ"
+
+
+@pytest.mark.parametrize("window", [0, 128, 3000])
+def test_decode_host_order_is_invisible(window):
+    """Work ordered on the host from a copy of kv_len (right or wrong) and by
+    the kernels' own ranking give bitwise identical results; the planned path
+    meets the parity bar."""
+    w = wl.paged_decode(batch=40, max_len=3000)
+    d = DeviceWorkload(w)
+    ro, rl = oracle_full(w, window)
+    for s in [1, 4]:
+        say(f"decode host order window={window} S={s}")
+        base = d.decode(s, window=window)
+        for name, host in _host_copies(w).items():
+            got = d.decode(s, window=window, kv_len_host=host)
+            _same(got, base, f"decode host copy {name} W={window} S={s}")
+        assert_parity(to_host(got[0]), ro, f"decode planned W={window} S={s}", to_host(got[1]), rl)
+
+
+def test_decode_host_order_large_batch_and_noalloc():
+    """Above 256 requests the host copy is ignored; the no-allocation entry
+    point takes it like the allocating one."""
+    rng = np.random.default_rng(32)
+    kv_len = rng.integers(1, 300, size=300)
+    w = wl.make_paged("big_batch", kv_len, np.ones(300), 16, 2, rng=rng, decode=True)
+    d = DeviceWorkload(w)
+    say("decode B=300 with a host copy; noalloc with a host copy")
+    _same(d.decode(3, kv_len_host=w.kv_len), d.decode(3), "decode B=300 host copy")
+    v = wl.paged_decode(batch=24, max_len=2000)
+    e = DeviceWorkload(v)
+    for name, host in _host_copies(v).items():
+        a = sa.decode_paged_noalloc(e.q, e.k, e.v, e.kv_indptr, e.page_indices, e.kv_len, e.sinks, v.scale,
+                                    num_splits=4, return_lse=True, kv_len_host=host)
+        _same(a, e.decode(4), f"noalloc host copy {name}")
+
+
 # ---------------------------------------------------------------------------
 # several query rows per request (speculative verify) over paged KV
 # ---------------------------------------------------------------------------
@@ -374,6 +421,29 @@ def test_custom_mask_random_and_edges(heads, max_rows):
     po, pl = oracle.split_partials_ref(w.q, kv_cache(w), w.sinks, w.scale, 4, qo_indptr=w.qo_indptr,
                                        custom_mask=masks)
     assert_parity(to_host(o_part), po, f"mask partials {heads}", to_host(lse_part), pl)
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_verify_host_order_is_invisible(masked):
+    w = wl.verify_tree() if masked else wl.verify_decode(batch=24)
+    masks = w.meta.get("masks") if masked else None
+    d = DeviceWorkload(w)
+    for s in [1, 3]:
+        say(f"verify host order masked={masked} S={s}")
+        base = d.decode_multi(s, 8, masks=masks)
+        for name, host in _host_copies(w).items():
+            _same(d.decode_multi(s, 8, masks=masks, kv_len_host=host), base,
+                  f"verify host copy {name} masked={masked} S={s}")
+
+
+@pytest.mark.parametrize("window", [0, 128])
+def test_mixed_batch_host_order_is_invisible(window):
+    w = wl.mixed_batch(n_prefill=4, chunk=200, max_prefix=900, n_decode=30, max_decode_len=1500)
+    d = DeviceWorkload(w)
+    say(f"mixed host order window={window}")
+    base = d.prefill(window=window)
+    for name, host in _host_copies(w).items():
+        _same(d.prefill(window=window, kv_len_host=host), base, f"mixed host copy {name} W={window}")
 
 
 def test_chain_mask_is_the_causal_kernel():

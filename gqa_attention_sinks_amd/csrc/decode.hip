@@ -142,7 +142,11 @@ void decode_paged_kernel(DecodeArgs a) {
   const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
   const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
   const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
-  const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block
+  const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block (K)
+  // V is read in two contiguous kilobytes, 16 bytes a lane: keys lane / 8 and
+  // 8 + lane / 8, chunk lane % 8 (a page's V goes through LDS anyway; whole
+  // runs per load stream faster than the operand layout's 32-byte pieces)
+  const int v_key = lane >> 3, v_chunk = lane & 7;
   uint8_t* stage = smem + wave * kPageBytes;
 
   // The wave's page ids arrive as vector loads, one lane per page, and each
@@ -177,11 +181,11 @@ void decode_paged_kernel(DecodeArgs a) {
     if (p < wp1) {
       const size_t off = (size_t)page_id(p) * page_stride;
       const uint16_t* kp = kpool + off + lane_off;
-      const uint16_t* vp = vpool + off + lane_off;
+      const uint16_t* vp = vpool + off + 8 * lane;
       kc[0] = ldg16(kp);
       kc[1] = ldg16(kp + 8);
       vc[0] = ldg16(vp);
-      vc[1] = ldg16(vp + 8);
+      vc[1] = ldg16(vp + 8 * kHeadDim);   // keys 8..15
     }
   };
   load_page(wp0);
@@ -234,9 +238,10 @@ void decode_paged_kernel(DecodeArgs a) {
       v0[e] = bf16x2_to_f16x2(v0r[e]);
       v1[e] = bf16x2_to_f16x2(v1r[e]);
     }
-    if (p * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
-    *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp)) = v0;
-    *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp + 1)) = v1;
+    if (p * kPageSize + v_key >= n_k) v0 = u32x4{};
+    if (p * kPageSize + 8 + v_key >= n_k) v1 = u32x4{};
+    *reinterpret_cast<u32x4*>(stage + page_swizzle(v_key, v_chunk)) = v0;
+    *reinterpret_cast<u32x4*>(stage + page_swizzle(8 + v_key, v_chunk)) = v1;
     __asm__ volatile("" ::: "memory");
     // transposed read: lane (grp, j) addresses key 4*grp + j/4, dims 16*db + 4*(j%4)
     const int rkey = 4 * grp + (col >> 2);

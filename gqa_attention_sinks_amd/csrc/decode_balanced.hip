@@ -209,7 +209,10 @@ void decode_balanced_kernel(BalancedArgs a) {
     // lane-derived values, recomputed per piece from the lane id (see opaque)
     const int ln = opaque(__lane_id());
     const int t = 64 * wave + ln, col = ln & 15, grp = ln >> 4;
-    const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block
+    const int lane_off = col * kHeadDim + 16 * grp;   // this lane's 32 bytes of a page block (K)
+    // V in two contiguous kilobytes, 16 bytes a lane: keys ln / 8 and 8 + ln / 8,
+    // chunk ln % 8 (whole runs per load stream faster than 32-byte pieces)
+    const int v_key = ln >> 3, v_chunk = ln & 7;
     uint8_t* stage = sm.u.run.stage[wave];
 
     // Q of the piece's request (its load overlaps the page-id load issued
@@ -238,8 +241,8 @@ void decode_balanced_kernel(BalancedArgs a) {
       const size_t off = (size_t)id * page_stride;
       kc[0] = ldg16(kpool + off + lane_off);
       kc[1] = ldg16(kpool + off + lane_off + 8);
-      vc[0] = ldg16(vpool + off + lane_off);
-      vc[1] = ldg16(vpool + off + lane_off + 8);
+      vc[0] = ldg16(vpool + off + 8 * ln);
+      vc[1] = ldg16(vpool + off + 8 * ln + 8 * kHeadDim);   // keys 8..15
     };
     if (my_pages > 0) load_page(0);
     for (int k = 0; k < my_pages; ++k) {
@@ -295,9 +298,10 @@ void decode_balanced_kernel(BalancedArgs a) {
         v0[e] = bf16x2_to_f16x2(v0r[e]);
         v1[e] = bf16x2_to_f16x2(v1r[e]);
       }
-      if (pn * kPageSize + col >= n_k) { v0 = u32x4{}; v1 = u32x4{}; }
-      *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp)) = v0;
-      *reinterpret_cast<u32x4*>(stage + page_swizzle(col, 2 * grp + 1)) = v1;
+      if (pn * kPageSize + v_key >= n_k) v0 = u32x4{};
+      if (pn * kPageSize + 8 + v_key >= n_k) v1 = u32x4{};
+      *reinterpret_cast<u32x4*>(stage + page_swizzle(v_key, v_chunk)) = v0;
+      *reinterpret_cast<u32x4*>(stage + page_swizzle(8 + v_key, v_chunk)) = v1;
       __asm__ volatile("" ::: "memory");
       // transposed read: lane (grp, j) addresses key 4*grp + j/4, dims 16*db + 4*(j%4)
       const int rkey = 4 * grp + (col >> 2);

@@ -274,18 +274,19 @@ void prefill_kernel(PrefillArgs a) {
   const TileLanes tl = tile_lanes(lane);
   const uint32_t smem0 = (uint32_t)(size_t)lds_ptr<uint8_t>(smem);   // LDS byte address
 
-  // Staging: thread -> key tid/4, 32 bytes at dims 16*(tid%4) of K and of V.
-  // A wave's sixteen keys are consecutive and share a page, so the address is
-  // a uniform base (scalar registers) plus a fixed per-lane offset.  Keys past
-  // the last one re-read the last key and are zeroed when staged, so the
-  // common full tile carries no per-row checks.
-  const int ld_key = tid >> 2;
-  const int ld_c = (tid & 3) * 2;   // first 16-byte chunk
+  // Staging: a wave stages sixteen consecutive keys (they share a page), each
+  // load a contiguous kilobyte of rows: lane -> keys lane/8 and 8 + lane/8,
+  // 16 bytes at chunk lane%8 of K and of V.  The address is a uniform base
+  // (scalar registers) plus a fixed per-lane offset.  Keys past the last one
+  // re-read the last key and are zeroed when staged, so the common full tile
+  // carries no per-row checks.
   const int wkey = 16 * wave;       // first key of this wave's rows
-  const int lkey = lane >> 2;       // this lane's key among them
+  const int lkey = lane >> 3;       // this lane's first key among them (the second: lkey + 8)
+  const int ld_c = lane & 7;        // this lane's 16-byte chunk
   const int32_t* page_list = PAGED ? a.page_indices + a.kv_indptr[b] : nullptr;
   const uint32_t key_bytes = PAGED ? kHeadDim * 2 : (uint32_t)a.num_kv_heads * kHeadDim * 2;
   const uint32_t lane_off_full = (uint32_t)lkey * key_bytes + ld_c * 16;
+  const uint32_t half_off = 8 * key_bytes;   // keys 8..15 of the wave
   const uint8_t* kbytes = reinterpret_cast<const uint8_t*>(a.k);
   const uint8_t* vbytes = reinterpret_cast<const uint8_t*>(a.v);
   // paged: the page holding the wave's first (clamped) key, fetched a tile ahead
@@ -296,34 +297,37 @@ void prefill_kernel(PrefillArgs a) {
     const int k0 = min(kt + wkey, n_k - 1);
     const size_t base = PAGED ? ((size_t)page * a.num_kv_heads + g) * (kPageSize * kHeadDim * 2)
                               : ((size_t)(kv_begin + k0) * a.num_kv_heads + g) * (kHeadDim * 2);
-    uint32_t off = lane_off_full;
+    uint32_t off0 = lane_off_full, off1 = lane_off_full + half_off;
     if (kt + kBN > n_k) {            // uniform: only the range's last tile
       __asm__ volatile("");
-      const int key = min(kt + wkey + lkey, n_k - 1);
-      off = (uint32_t)(PAGED ? key % kPageSize : key - k0) * key_bytes + ld_c * 16;
+      const int key0 = min(kt + wkey + lkey, n_k - 1);
+      const int key1 = min(kt + wkey + 8 + lkey, n_k - 1);
+      off0 = (uint32_t)(PAGED ? key0 % kPageSize : key0 - k0) * key_bytes + ld_c * 16;
+      off1 = (uint32_t)(PAGED ? key1 % kPageSize : key1 - k0) * key_bytes + ld_c * 16;
     }
-    kr[0] = *reinterpret_cast<const u32x4*>(kbytes + base + off);
-    kr[1] = *reinterpret_cast<const u32x4*>(kbytes + base + off + 16);
-    vr[0] = *reinterpret_cast<const u32x4*>(vbytes + base + off);
-    vr[1] = *reinterpret_cast<const u32x4*>(vbytes + base + off + 16);
+    kr[0] = *reinterpret_cast<const u32x4*>(kbytes + base + off0);
+    kr[1] = *reinterpret_cast<const u32x4*>(kbytes + base + off1);
+    vr[0] = *reinterpret_cast<const u32x4*>(vbytes + base + off0);
+    vr[1] = *reinterpret_cast<const u32x4*>(vbytes + base + off1);
   };
   auto store_tile = [&](int stage, int kt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
     uint8_t* ks = smem + stage * 2 * kTileBytes;
     uint8_t* vs = ks + kTileBytes;
     if (kt + kBN > n_k) {            // uniform: only the range's last tile
       __asm__ volatile("");
-      if (kt + ld_key >= n_k) kr[0] = kr[1] = vr[0] = vr[1] = u32x4{};
+      if (kt + wkey + lkey >= n_k) kr[0] = vr[0] = u32x4{};
+      if (kt + wkey + 8 + lkey >= n_k) kr[1] = vr[1] = u32x4{};
     }
-    *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c)) = kr[0];
-    *reinterpret_cast<u32x4*>(ks + tile_swizzle(ld_key, ld_c + 1)) = kr[1];
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + lkey, ld_c)) = kr[0];
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + 8 + lkey, ld_c)) = kr[1];
     // V is staged as fp16: the weights of the P.V product are fp16
     u32x4 v16[2];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) v16[u][e] = bf16x2_to_f16x2(vr[u][e]);
-    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c)) = v16[0];
-    *reinterpret_cast<u32x4*>(vs + tile_swizzle(ld_key, ld_c + 1)) = v16[1];
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(wkey + lkey, ld_c)) = v16[0];
+    *reinterpret_cast<u32x4*>(vs + tile_swizzle(wkey + 8 + lkey, ld_c)) = v16[1];
   };
 
   int pid = 0;

@@ -195,7 +195,12 @@ void verify_kernel(DecodeArgs a) {
   const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
   const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
   const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
-  const int lane_off = (r32 & 15) * kHeadDim + 8 * half;            // key r32 of the step, 8-dim slice
+  const int lane_off = (r32 & 15) * kHeadDim + 8 * half;            // K: key r32 of the step, 8-dim slice
+  // V is read in contiguous kilobytes, 16 bytes a lane: load j holds key
+  // 8 j + lane / 8 of the step (page a for j < 2, else page b), chunk
+  // lane % 8 (V goes through LDS anyway; whole runs per load stream faster
+  // than the operand layout's 16-byte pieces)
+  const int v_key = lane >> 3, v_chunk = lane & 7;
   uint8_t* stage = sm.u.run.stage[wave];
   const uint32_t stage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)stage;
   const TileLanes tl = tile_lanes(lane);
@@ -242,7 +247,7 @@ void verify_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       kc[ks] = ldg16(kpool + off + 16 * ks);
-      vc[ks] = ldg16(vpool + off + 16 * ks);
+      vc[ks] = ldg16(vpool + (size_t)(ks < 2 ? id_a : id_b) * page_stride + (ks & 1) * 8 * kHeadDim + 8 * lane);
     }
   };
 
@@ -252,6 +257,9 @@ void verify_kernel(DecodeArgs a) {
       __attribute__((always_inline)) {
     const int p = wp0 + 2 * st;
     const int key_base = p * kPageSize;
+    // the next step's pages, into the set the previous step has finished with
+    advance_ids(min(p + 2, p_last));
+    load_step(p + 2, kn, vn);
     // scores of the step, every column block the request fills
     f32x16 s[2];
 #pragma unroll
@@ -266,20 +274,15 @@ void verify_kernel(DecodeArgs a) {
     }
     // V of the step as fp16 into the wave's stage; rows past the wave's keys
     // are zeroed so that no stale or poisoned value meets a zero weight
-    {
-      const bool key_ok = key_base + r32 < run_end;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v16;
+    for (int j = 0; j < 4; ++j) {
+      const bool key_ok = key_base + 8 * j + v_key < run_end;
+      u32x4 v16;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v16[e] = key_ok ? bf16x2_to_f16x2(vc[ks][e]) : 0u;
-        *reinterpret_cast<u32x4*>(stage + tile_swizzle(r32, 2 * ks + half)) = v16;
-      }
+      for (int e = 0; e < 4; ++e) v16[e] = key_ok ? bf16x2_to_f16x2(vc[j][e]) : 0u;
+      *reinterpret_cast<u32x4*>(stage + tile_swizzle(8 * j + v_key, v_chunk)) = v16;
     }
     __asm__ volatile("" ::: "memory");
-    // the next step's pages
-    advance_ids(min(p + 2, p_last));
-    load_step(p + 2, kn, vn);
 
     // visibility: the common step shows every key to every real column
     const bool step_in = key_base >= t_lo && key_base + kStepKeys <= run_end;

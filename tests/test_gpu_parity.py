@@ -304,6 +304,22 @@ def test_decode_host_order_is_invisible(window):
         assert_parity(to_host(got[0]), ro, f"decode planned W={window} S={s}", to_host(got[1]), rl)
 
 
+@pytest.mark.parametrize("batch,window", [(2, 0), (256, 0), (257, 0), (40, 2048), (40, 2049)])
+def test_decode_host_order_at_its_limits(batch, window):
+    """The host order applies to batches of 2..256 requests and windows of
+    none or over 2048 keys; at and across each limit the results equal the
+    kernels' own ordering bit for bit."""
+    rng = np.random.default_rng(batch * 7 + window)
+    kv_len = rng.integers(1, 2600, size=batch)
+    w = wl.make_paged("order_limits", kv_len, np.ones(batch), 16, 2, rng=rng, decode=True)
+    d = DeviceWorkload(w)
+    say(f"decode host order limits batch={batch} window={window}")
+    for s in [1, 3]:
+        base = d.decode(s, window=window)
+        for name, host in _host_copies(w).items():
+            _same(d.decode(s, window=window, kv_len_host=host), base, f"B={batch} W={window} S={s} {name}")
+
+
 def test_decode_host_order_large_batch_and_noalloc():
     """Above 256 requests the host copy is ignored; the no-allocation entry
     point takes it like the allocating one."""

@@ -126,6 +126,28 @@ void verify_kernel(DecodeArgs a) {
   const int full_lo = a.window > 0 ? max(t_lo, n_k - a.window) : t_lo;
   const int full_hi = min(t_hi - 1, n_k - n_q);
 
+  const int32_t* pages = a.page_indices + __builtin_amdgcn_readfirstlane(du.page_base);
+  const size_t head_stride = (size_t)kPageSize * kHeadDim;          // elements per (page, KV head)
+  const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
+  const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
+  const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
+  const int lane_off = (r32 & 15) * kHeadDim + 8 * half;            // K: key r32 of the step, 8-dim slice
+  // V is read in contiguous kilobytes, 16 bytes a lane: load j holds key
+  // 8 j + lane / 8 of the step (page a for j < 2, else page b), chunk
+  // lane % 8 (V goes through LDS anyway; whole runs per load stream faster
+  // than the operand layout's 16-byte pieces)
+  const int v_key = lane >> 3, v_chunk = lane & 7;
+  uint8_t* stage = sm.u.run.stage[wave];
+  const uint32_t stage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)stage;
+  const TileLanes tl = tile_lanes(lane);
+
+  // Page ids of the wave's run arrive as vector loads, one lane per page, in
+  // two registers of 64 (even and odd groups); entering group g reloads the
+  // register of group g - 1 with group g + 1, 64 pages ahead of its use.
+  // They go out first: the first pages wait for them.
+  int ids0 = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
+  int ids1 = 64 + lane < wp1 - wp0 ? pages[wp0 + 64 + lane] : 0;
+
   // Q^T operands: entry [cb][ks][l] holds column 32 cb + l % 32, dims
   // 16 ks + 8 (l / 32) .. + 7 (zero for columns past the request's rows)
   for (int e = tid; e < 2 * 4 * 64; e += kVThreads) {
@@ -149,6 +171,50 @@ void verify_kernel(DecodeArgs a) {
     v_hi[cb] = t < n_q ? (MASK ? t_hi - 1 : min(t_hi - 1, c_pos)) : -1;   // a column past the rows sees nothing
     c_bit[cb] = t < n_q ? t * n_k : -1;
   }
+  int next_group = 1;
+  auto page_id = [&](int p) -> int {      // p uniform, in the current group or the next
+    const int r = p - wp0;
+    return ((r >> 6) & 1) ? __builtin_amdgcn_readlane(ids1, r & 63) : __builtin_amdgcn_readlane(ids0, r & 63);
+  };
+  auto advance_ids = [&](int p) {         // p: the first page of the step being processed
+    const int gr = (p - wp0) >> 6;
+    if (gr == next_group) {
+      ++next_group;
+      const int base = wp0 + 64 * (gr + 1);
+      if (gr & 1) ids0 = base + lane < wp1 ? pages[base + lane] : 0;
+      else ids1 = base + lane < wp1 ? pages[base + lane] : 0;
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
+  };
+  // The step at page p: K of key l % 32 (page p or p + 1; past the run the
+  // last page again) in the operand layout, V in contiguous rows.  Two
+  // register sets alternate between steps: each step first loads the next
+  // step's pages into the set the previous step has finished with, so they
+  // are in flight while it computes (a third set, two steps ahead, measured
+  // slower: more pages in flight cost more than the latency they hide).
+  // Every path issues the same loads (a step past the run reloads the run's
+  // last pages, a cache hit): the compiler's count of loads in flight then
+  // stays exact, and a step waits for its own pages only.
+  const int n_steps = (wp1 - wp0 + 1) / 2;
+  const int p_last = wp0 + 2 * max(n_steps - 1, 0);    // the run's last step
+  u32x4 kA[4], vA[4], kB[4], vB[4];
+  auto load_step = [&](int p, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
+    p = min(p, p_last);
+    const int id_a = page_id(p);
+    const int id_b = page_id(min(p + 1, wp1 - 1));
+    const int id = (r32 >> 4) ? id_b : id_a;
+    const size_t off = (size_t)id * page_stride + lane_off;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      kc[ks] = ldg16(kpool + off + 16 * ks);
+      vc[ks] = ldg16(vpool + (size_t)(ks < 2 ? id_a : id_b) * page_stride + (ks & 1) * 8 * kHeadDim + 8 * lane);
+    }
+  };
+
+  // the ids (and Q) have arrived: the first step's pages go out now, so
+  // that they are in flight during the mask scan
+  __builtin_amdgcn_s_waitcnt(kWaitVm0);
+  if (n_steps > 0) load_step(wp0, kA, vA);
   const uint8_t* mbytes = MASK ? a.custom_mask + a.mask_indptr[b] : nullptr;
   // MASK: per row, the first hidden key of the chunk (t_hi when none).  The
   // steps below it show all their keys to that row, so only the others read
@@ -190,68 +256,6 @@ void verify_kernel(DecodeArgs a) {
   f32x16 acc[2][2] = {};   // [column block][dim block]
   const float cs = a.scale_log2;
 
-  const int32_t* pages = a.page_indices + __builtin_amdgcn_readfirstlane(du.page_base);
-  const size_t head_stride = (size_t)kPageSize * kHeadDim;          // elements per (page, KV head)
-  const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
-  const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
-  const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
-  const int lane_off = (r32 & 15) * kHeadDim + 8 * half;            // K: key r32 of the step, 8-dim slice
-  // V is read in contiguous kilobytes, 16 bytes a lane: load j holds key
-  // 8 j + lane / 8 of the step (page a for j < 2, else page b), chunk
-  // lane % 8 (V goes through LDS anyway; whole runs per load stream faster
-  // than the operand layout's 16-byte pieces)
-  const int v_key = lane >> 3, v_chunk = lane & 7;
-  uint8_t* stage = sm.u.run.stage[wave];
-  const uint32_t stage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)stage;
-  const TileLanes tl = tile_lanes(lane);
-
-  // Page ids of the wave's run arrive as vector loads, one lane per page, in
-  // two registers of 64 (even and odd groups); entering group g reloads the
-  // register of group g - 1 with group g + 1, 64 pages ahead of its use.
-  int ids0 = lane < wp1 - wp0 ? pages[wp0 + lane] : 0;
-  int ids1 = 64 + lane < wp1 - wp0 ? pages[wp0 + 64 + lane] : 0;
-  __builtin_amdgcn_s_waitcnt(kWaitVm0);
-  int next_group = 1;
-  auto page_id = [&](int p) -> int {      // p uniform, in the current group or the next
-    const int r = p - wp0;
-    return ((r >> 6) & 1) ? __builtin_amdgcn_readlane(ids1, r & 63) : __builtin_amdgcn_readlane(ids0, r & 63);
-  };
-  auto advance_ids = [&](int p) {         // p: the first page of the step being processed
-    const int gr = (p - wp0) >> 6;
-    if (gr == next_group) {
-      ++next_group;
-      const int base = wp0 + 64 * (gr + 1);
-      if (gr & 1) ids0 = base + lane < wp1 ? pages[base + lane] : 0;
-      else ids1 = base + lane < wp1 ? pages[base + lane] : 0;
-      __builtin_amdgcn_s_waitcnt(kWaitVm0);
-    }
-  };
-  // The step at page p: lane l reads key l % 32 (page p or p + 1; past the
-  // run the last page again), 16 bytes of K and of V per k step.  Two
-  // register sets alternate between steps: the next step's pages go to the
-  // other set once the current step's V is staged, so they are in flight
-  // while it computes (two steps ahead, refilling the set a step frees,
-  // measured slower: 75.4 against 69.5 us on the verify batch).  Every path
-  // issues the same loads (a step past the run reloads the run's last pages,
-  // a cache hit): the compiler's count of loads in flight then stays exact,
-  // and a step waits for its own pages only.
-  const int n_steps = (wp1 - wp0 + 1) / 2;
-  const int p_last = wp0 + 2 * max(n_steps - 1, 0);    // the run's last step
-  u32x4 kA[4], vA[4], kB[4], vB[4];
-  auto load_step = [&](int p, u32x4 (&kc)[4], u32x4 (&vc)[4]) {
-    p = min(p, p_last);
-    const int id_a = page_id(p);
-    const int id_b = page_id(min(p + 1, wp1 - 1));
-    const int id = (r32 >> 4) ? id_b : id_a;
-    const size_t off = (size_t)id * page_stride + lane_off;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      kc[ks] = ldg16(kpool + off + 16 * ks);
-      vc[ks] = ldg16(vpool + (size_t)(ks < 2 ? id_a : id_b) * page_stride + (ks & 1) * 8 * kHeadDim + 8 * lane);
-    }
-  };
-
-  if (n_steps > 0) load_step(wp0, kA, vA);
   // step st with its pages in (kc, vc); (kn, vn): the other set
   auto step = [&](const int st, u32x4 (&kc)[4], u32x4 (&vc)[4], u32x4 (&kn)[4], u32x4 (&vn)[4])
       __attribute__((always_inline)) {

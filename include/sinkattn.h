@@ -124,7 +124,8 @@ typedef struct sinkattn_kv {
    * the buffers that configure and schedule the attention kernel for each
    * batch).  It only orders the work: the results are
    * the same whatever it holds (the lengths the kernels use are always the
-   * device kv_len's). */
+   * device kv_len's).  sinkattn_decode_paged_balanced plans its segments on
+   * the device and does not read it. */
   const int32_t* kv_len_host;
 } sinkattn_kv;
 

@@ -50,6 +50,27 @@ def test_abi_version(lib):
     assert lib.sinkattn_status_string(2) == b"unsupported"
 
 
+def test_kv_descriptor_layout_matches_the_header(tmp_path):
+    """The ctypes mirror of sinkattn_kv has the C struct's size and field
+    offsets (a C program built against include/sinkattn.h prints them)."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    fields = [f for f, _ in binding._KV._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "sinkattn.h"\nint main(void) {\n'
+                   '  printf("%zu", sizeof(sinkattn_kv));\n'
+                   + "".join(f'  printf(" %zu", offsetof(sinkattn_kv, {f}));\n' for f in fields)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    subprocess.run([cc, "-std=c99", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split()]
+    want = [ctypes.sizeof(binding._KV)] + [getattr(binding._KV, f).offset for f in fields]
+    assert got == want, (got, want)
+
+
 def test_split_rule_matches_oracle_exactly(lib):
     rng = np.random.default_rng(123)
     all_lens = np.arange(0, 4097, dtype=np.int32)

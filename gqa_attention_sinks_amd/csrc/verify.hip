@@ -18,8 +18,9 @@
 //   blocks (the second one skipped, wave-uniformly, when the request has at
 //   most 32 columns).  Per step of two pages (32 keys) and column block:
 //     S^T[32 keys x 32 cols] = K . Q^T        -> 4 x MFMA 32x32x16 bf16
-//       K goes straight from HBM into the A operand (lane l: key l % 32, dims
-//       16 ks + 8 (l / 32) .. + 7); the Q^T operands are staged in LDS once
+//       K is read in contiguous rows, staged per wave in LDS and read back in
+//       the A operand layout (lane l: key l % 32, dims 16 ks + 8 (l / 32)
+//       .. + 7); the Q^T operands are staged in LDS once
 //     weights exp2(s c - m) against a reference per column that moves only
 //     when some weight would pass 2^14 (then: the column maxima, a rescale
 //     and the weights again), summed from the same fp16 values that feed P.V
@@ -61,7 +62,8 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 struct VerifySmem {
   union {
     struct {
-      uint8_t stage[kVW][kStageBytes];
+      uint8_t stage[kVW][kStageBytes];    // V of the wave's step, fp16
+      uint8_t kstage[kVW][kStageBytes];   // K of the wave's step, bf16
       u32x4 q[2][4][64];                 // [column block][k step][lane]
     } run;
     struct {
@@ -131,13 +133,15 @@ void verify_kernel(DecodeArgs a) {
   const size_t page_stride = (size_t)a.num_kv_heads * head_stride;  // elements per page
   const uint16_t* kpool = a.k_pool + (size_t)g * head_stride;
   const uint16_t* vpool = a.v_pool + (size_t)g * head_stride;
-  const int lane_off = (r32 & 15) * kHeadDim + 8 * half;            // K: key r32 of the step, 8-dim slice
-  // V is read in contiguous kilobytes, 16 bytes a lane: load j holds key
-  // 8 j + lane / 8 of the step (page a for j < 2, else page b), chunk
-  // lane % 8 (V goes through LDS anyway; whole runs per load stream faster
-  // than the operand layout's 16-byte pieces)
+  // K and V are read in contiguous kilobytes, 16 bytes a lane: load j holds
+  // key 8 j + lane / 8 of the step (page a for j < 2, else page b), chunk
+  // lane % 8; both go through LDS (whole runs per load stream faster than the
+  // operand layout's 16-byte pieces: 65.8 against 59.1 us for the loads alone
+  // on the verify batch)
   const int v_key = lane >> 3, v_chunk = lane & 7;
   uint8_t* stage = sm.u.run.stage[wave];
+  uint8_t* kstage = sm.u.run.kstage[wave];
+  const uint32_t kstage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)kstage;
   const uint32_t stage0 = (uint32_t)(size_t)(__attribute__((address_space(3))) uint8_t*)stage;
   const TileLanes tl = tile_lanes(lane);
 
@@ -186,8 +190,8 @@ void verify_kernel(DecodeArgs a) {
       __builtin_amdgcn_s_waitcnt(kWaitVm0);
     }
   };
-  // The step at page p: K of key l % 32 (page p or p + 1; past the run the
-  // last page again) in the operand layout, V in contiguous rows.  Two
+  // The step at page p: K and V of pages p and p + 1 (past the run the last
+  // page again) in contiguous rows.  Two
   // register sets alternate between steps: each step first loads the next
   // step's pages into the set the previous step has finished with, so they
   // are in flight while it computes (a third set, two steps ahead, measured
@@ -202,12 +206,11 @@ void verify_kernel(DecodeArgs a) {
     p = min(p, p_last);
     const int id_a = page_id(p);
     const int id_b = page_id(min(p + 1, wp1 - 1));
-    const int id = (r32 >> 4) ? id_b : id_a;
-    const size_t off = (size_t)id * page_stride + lane_off;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      kc[ks] = ldg16(kpool + off + 16 * ks);
-      vc[ks] = ldg16(vpool + (size_t)(ks < 2 ? id_a : id_b) * page_stride + (ks & 1) * 8 * kHeadDim + 8 * lane);
+    for (int j = 0; j < 4; ++j) {
+      const size_t off = (size_t)(j < 2 ? id_a : id_b) * page_stride + (j & 1) * 8 * kHeadDim + 8 * lane;
+      kc[j] = ldg16(kpool + off);
+      vc[j] = ldg16(vpool + off);
     }
   };
 
@@ -264,6 +267,14 @@ void verify_kernel(DecodeArgs a) {
     // the next step's pages, into the set the previous step has finished with
     advance_ids(min(p + 2, p_last));
     load_step(p + 2, kn, vn);
+    // K of the step through the wave's LDS stage: rows in, operand layout out
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<u32x4*>(kstage + tile_swizzle(8 * j + v_key, v_chunk)) = kc[j];
+    __asm__ volatile("" ::: "memory");
+    bf16x8 kop[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) kop[ks] = *lds_at<const bf16x8>(kstage0 + tl.k[ks]);
     // scores of the step, every column block the request fills
     f32x16 s[2];
 #pragma unroll
@@ -272,7 +283,7 @@ void verify_kernel(DecodeArgs a) {
       if (cb >= nb_used) continue;
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, kc[ks]),
+        s[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop[ks],
                                                         __builtin_bit_cast(bf16x8, sm.u.run.q[cb][ks][lane]),
                                                         s[cb], 0, 0, 0);
     }

@@ -305,6 +305,9 @@ void decode_paged_kernel(DecodeArgs a) {
   }
 }
 
+// (row, head) pairs from which a merge launch packs four pairs into a wave.
+constexpr long kMerge4MinPairs = 8192;
+
 // One wave per (row, head); lane = output dimension.  With at most N chunks
 // (N = 4, 8 or 16, the smallest that fits) every load -- the chunk LSEs and
 // this lane's value of each partial -- is issued before the first use, so
@@ -365,6 +368,77 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (a.lse != nullptr && lane == 0) a.lse[rh] = den > 0.f ? mx + __builtin_logf(den) : mx;
 }
 
+// One (row, head) per sixteen lanes, four output dimensions a lane.  With at
+// most N chunks (N = 4, 8 or 16, the smallest that fits) every load -- the
+// chunk LSEs and this lane's four values of each partial -- is issued before
+// the first use, so the wave waits for one memory round trip instead of one
+// per chunk; more chunks take the plain loop.
+template <int N>
+__device__ __forceinline__ void merge_regs4(const float* lp, const f32x4* op, int S, float& mx,
+                                           float& den, f32x4& num) {
+  float l[N];
+  f32x4 o[N];
+#pragma unroll
+  for (int c = 0; c < N; ++c) {   // index clamped to chunk S - 1: straight-line loads
+    const int cc = min(c, S - 1);
+    l[c] = lp[cc];
+    o[c] = op[(long)cc * (kHeadDim / 4)];
+  }
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (c >= S) l[c] = kNegInf;
+    mx = fmaxf(mx, l[c]);
+  }
+  if (mx == kNegInf) return;
+#pragma unroll
+  for (int c = 0; c < N; ++c) {
+    if (c >= S) break;
+    const float wt = (l[c] == mx) ? 1.f : exp2_hw((l[c] - mx) * kLog2e);
+    den += wt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) num[e] += wt * o[c][e];
+  }
+}
+
+// Four (row, head) pairs per wave, for launches with many pairs (one wave per
+// pair left the verify batch's 21k pairs in three rounds of waves; with few
+// pairs and many chunks, one pair per wave keeps more waves loading).
+__global__ __launch_bounds__(256) void merge4_kernel(MergeArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long rh = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * 4 + (lane >> 4);
+  if (rh >= (long)a.rows * a.num_heads) return;
+  const int d0 = 4 * (lane & 15);
+  const int S = a.num_splits;
+  const float* lp = a.lse_part + rh * S;
+  const f32x4* op = reinterpret_cast<const f32x4*>(a.o_part + rh * S * kHeadDim + d0);
+  float mx = kNegInf, den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  if (S <= 4) {
+    merge_regs4<4>(lp, op, S, mx, den, num);
+  } else if (S <= 8) {
+    merge_regs4<8>(lp, op, S, mx, den, num);
+  } else if (S <= 16) {
+    merge_regs4<16>(lp, op, S, mx, den, num);
+  } else {
+    for (int c = 0; c < S; ++c) mx = fmaxf(mx, lp[c]);
+    if (mx != kNegInf) {
+      for (int c = 0; c < S; ++c) {
+        const float l = lp[c];
+        const float wt = (l == mx) ? 1.f : exp2_hw((l - mx) * kLog2e);
+        den += wt;
+        const f32x4 o = op[(long)c * (kHeadDim / 4)];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) num[e] += wt * o[e];
+      }
+    }
+  }
+  uint32_t h[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) h[e] = to_bf16_bits(den > 0.f ? num[e] / den : 0.f);
+  *reinterpret_cast<u32x2*>(a.out + rh * kHeadDim + d0) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  if (a.lse != nullptr && (lane & 15) == 0) a.lse[rh] = den > 0.f ? mx + __builtin_logf(den) : mx;
+}
+
 }  // namespace
 
 // One-row decode: four waves per workgroup, one page in flight per wave (the
@@ -380,7 +454,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream) {
   const long n = (long)a.rows * a.num_heads;
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, a);
+  if (n >= kMerge4MinPairs)
+    hipLaunchKernelGGL(merge4_kernel, dim3((unsigned)((n + 15) / 16)), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(merge_kernel, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -493,3 +493,27 @@ def test_merge_entry_point():
     ro, rl = oracle.merge_ref(o, l)
     assert_parity(to_host(out)[1:], ro[1:], "merge", to_host(lse), rl)
     assert np.all(to_host(out)[0, 0] == 0)
+
+
+@pytest.mark.parametrize("rows,heads,s", [(127, 64, 3), (129, 64, 3), (129, 64, 17), (520, 64, 2), (135, 61, 4)])
+def test_merge_both_launch_shapes(rows, heads, s):
+    """Launches of 8192 (row, head) pairs or more pack four pairs into a
+    wave, smaller ones one: both against the oracle, with empty, sink-only and
+    dominant chunks among the inputs, and a ragged last group of pairs."""
+    import torch
+    rng = np.random.default_rng(rows * 31 + heads * 7 + s)
+    o = rng.normal(size=(rows, heads, s, 64)).astype(np.float32)
+    l = rng.normal(0, 3, size=(rows, heads, s)).astype(np.float32)
+    l[0, 0, :] = -np.inf
+    o[0, 0, :] = 0
+    l[1, :, 1:] = -np.inf
+    l[2, 5, 0] = 40.0
+    l[rows - 1, heads - 1, s - 1] = 30.0
+    say(f"merge launch shapes rows={rows} heads={heads} S={s} pairs={rows * heads}")
+    dev = torch.device("cuda:0")
+    out, lse = sa.merge(torch.from_numpy(o).to(dev), torch.from_numpy(l).to(dev), return_lse=True)
+    ro, rl = oracle.merge_ref(o, l)
+    g, gl = to_host(out), to_host(lse)
+    assert np.all(g[0, 0] == 0) and gl[0, 0] == -np.inf
+    g[0, 0] = ro[0, 0] = 0
+    assert_parity(g, ro, f"merge rows={rows} heads={heads} S={s}", gl, rl)

@@ -400,15 +400,15 @@ __device__ __forceinline__ void merge_few(const float* lp, const float* op, size
 // a request without keys gets out = 0, lse = sink; the others merge their
 // pieces' partials (the LSE merge of split partials).  When every row has at
 // most 16 pieces each wave merges its own row with all loads issued first;
-// otherwise (a long request can have a piece in almost every segment) the
-// four waves share each row: the block-wide maximum of the pieces' LSEs, then
-// wave w sums pieces w, w + 4, ... and the sums are combined in LDS.
+// otherwise (a long request can have a piece in almost every segment) each
+// wave still takes its own row, its lanes split four ways over the pieces and
+// sixteen ways over the dimensions: lane l merges pieces l / 16 + 4 k (sixteen
+// a pass, every load issued first) on dimensions 4 (l % 16) .. + 3 into its
+// own (maximum, sum, accumulator), and the four groups combine by shuffles.
 constexpr int kMergeRows = 4;
 constexpr int kMergeThreads = 64 * kMergeRows;
 
 __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(BalancedArgs a) {
-  __shared__ float s_max[kMergeRows][kMergeRows];               // [wave][row]
-  __shared__ float s_sum[kMergeRows][kMergeRows][kHeadDim + 1];   // [wave][row][dims, den]
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const long rows = (long)a.batch * a.num_qo_heads;
@@ -459,44 +459,79 @@ __global__ __launch_bounds__(kMergeThreads) void merge_balanced_kernel(BalancedA
       else merge_few<16>(lp, op, stride, cnt[wave], mx, den, num);
     }
   } else {
+    // wave = row; lane = (piece group lane / 16, dimension quad lane % 16):
+    // the lane merges pieces lane / 16 + 4 k on dimensions 4 (lane % 16) .. + 3,
+    // sixteen pieces a pass with every load issued first
+    const int pg = lane >> 4, dq = lane & 15;
+    float m_t = kNegInf, d_t = 0.f;
+    f32x4 n_t = {0.f, 0.f, 0.f, 0.f};
+    const int cw = cnt[wave];
+    if (cw > 0) {
+      const long rhw = (long)blockIdx.x * kMergeRows + wave;
+      const int r = (int)(rhw / a.num_qo_heads), h = (int)(rhw % a.num_qo_heads);
+      const float* lp = a.ws_lse + (size_t)(s0v[wave] + r) * stride + h;
+      const f32x4* op4 = reinterpret_cast<const f32x4*>(a.ws_o + ((size_t)(s0v[wave] + r) * stride + h) * kHeadDim) + dq;
+      for (int i0 = pg; i0 < cw; i0 += 4 * 16) {
+        // a slot no workgroup wrote may hold anything (the kernels are built
+        // assuming no NaN), so an entry past the row's pieces or in an empty
+        // segment reads the row's first piece, always written, and weighs 0
+        bool ok[16];
+        float l[16];
+        f32x4 o[16];
 #pragma unroll
-    for (int j = 0; j < kMergeRows; ++j) {
-      float m = kNegInf;
-      if (cnt[j] > 0) {
-        const float *lp, *op;
-        slot_ptrs(j, &lp, &op);
-        for (int i = tid; i < cnt[j]; i += kMergeThreads)
-          if (held(j, i)) m = fmaxf(m, lp[(size_t)i * stride]);
-      }
+        for (int u = 0; u < 16; ++u) {
+          const int i = i0 + 4 * u;
+          ok[u] = i < cw && held(wave, i);
+          const size_t ii = ok[u] ? (size_t)i : 0;
+          l[u] = lp[ii * stride];
+          o[u] = op4[ii * stride * (kHeadDim / 4)];
+        }
+        float m_new = m_t;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, shfl_xor_f32(m, off));
-      if (lane == 0) s_max[wave][j] = m;
-    }
-    __syncthreads();
+        for (int u = 0; u < 16; ++u)
+          if (ok[u]) m_new = fmaxf(m_new, l[u]);
+        if (m_new == kNegInf) continue;
+        const float alpha = (m_t == m_new) ? 1.f : exp2_hw((m_t - m_new) * kLog2e);
+        d_t *= alpha;
 #pragma unroll
-    for (int j = 0; j < kMergeRows; ++j) {
-      const float mj = fmaxf(fmaxf(s_max[0][j], s_max[1][j]), fmaxf(s_max[2][j], s_max[3][j]));
-      float dj = 0.f, nj = 0.f;
-      if (cnt[j] > 0 && mj != kNegInf) {
-        const float *lp, *op;
-        slot_ptrs(j, &lp, &op);
-#pragma unroll 4
-        for (int i = wave; i < cnt[j]; i += kMergeRows) {
-          if (!held(j, i)) continue;
-          const float l = lp[(size_t)i * stride];
-          const float wt = (l == mj) ? 1.f : exp2_hw((l - mj) * kLog2e);
-          dj += wt;
-          nj += wt * op[(size_t)i * stride * kHeadDim];
+        for (int e = 0; e < 4; ++e) n_t[e] *= alpha;
+        m_t = m_new;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          float wt = (l[u] == m_t) ? 1.f : exp2_hw((l[u] - m_t) * kLog2e);
+          wt = ok[u] ? wt : 0.f;
+          d_t += wt;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) n_t[e] += wt * o[u][e];
         }
       }
-      s_sum[wave][j][lane] = nj;
-      if (lane == 0) s_sum[wave][j][kHeadDim] = dj;
-      if (j == wave) mx = mj;
     }
-    __syncthreads();
-    num = s_sum[0][wave][lane] + s_sum[1][wave][lane] + s_sum[2][wave][lane] + s_sum[3][wave][lane];
-    den = s_sum[0][wave][kHeadDim] + s_sum[1][wave][kHeadDim] + s_sum[2][wave][kHeadDim] +
-          s_sum[3][wave][kHeadDim];
+    // the four piece groups of the wave (lanes l, l ^ 16, l ^ 32, l ^ 48 hold
+    // one dimension quad) combine by the LSE rule
+    float mw = fmaxf(m_t, shfl_xor_f32(m_t, 16));
+    mw = fmaxf(mw, shfl_xor_f32(mw, 32));
+    const float sc = (m_t == kNegInf) ? 0.f : ((m_t == mw) ? 1.f : exp2_hw((m_t - mw) * kLog2e));
+    float dw = d_t * sc;
+    dw += shfl_xor_f32(dw, 16);
+    dw += shfl_xor_f32(dw, 32);
+    f32x4 nw;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      nw[e] = n_t[e] * sc;
+      nw[e] += shfl_xor_f32(nw[e], 16);
+      nw[e] += shfl_xor_f32(nw[e], 32);
+    }
+    if (cw > 0) {
+      const long rhw = (long)blockIdx.x * kMergeRows + wave;
+      if (pg == 0) {
+        uint32_t hb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hb[e] = to_bf16_bits(dw > 0.f ? nw[e] / dw : 0.f);
+        *reinterpret_cast<u32x2*>(a.out + rhw * kHeadDim + 4 * dq) = u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)};
+        if (a.lse != nullptr && dq == 0) a.lse[rhw] = dw > 0.f ? mw + __builtin_logf(dw) : mw;
+      }
+      return;
+    }
   }
 
   // wave j writes row j

@@ -1,7 +1,10 @@
 """The entry points are documented as safe to capture in a HIP graph: they
 allocate nothing, never synchronise the host and keep no device state
-between calls.  Capture split decode + merge, prefill and a verify call
-into one graph, replay it several times with eager work in between, and
+between calls.  Capture split decode + merge (also with the work ordered
+from a host copy of kv_len), the balanced decode + its merge, prefill and
+two verify calls (the second large enough for the merge that packs four
+(row, head) pairs a wave) into one graph, replay it several times with eager
+work in between, and
 check every replay against the eager results bit for bit; the same for the
 append with rotary embedding and the MoE routing."""
 
@@ -30,13 +33,20 @@ def test_graph_replay_matches_eager():
     pre = DeviceWorkload(wl.make_contiguous("graph_prefill", [300, 129], [300, 64], 16, 2,
                                             rng=np.random.default_rng(4)))
     ver = DeviceWorkload(wl.verify_decode(batch=12, max_len=900))
-    dw, pw, vw = dec.w, pre.w, ver.w
+    big = DeviceWorkload(wl.verify_decode())          # 327 rows x 64 heads: the four-pairs-a-wave merge
+    dw, pw, vw, bw = dec.w, pre.w, ver.w, big.w
 
-    outs = dict(dec=torch.empty_like(dec.q), pre=torch.empty_like(pre.q), ver=torch.empty_like(ver.q))
+    outs = dict(dec=torch.empty_like(dec.q), pre=torch.empty_like(pre.q), ver=torch.empty_like(ver.q),
+                big=torch.empty_like(big.q), bal=torch.empty_like(dec.q), host=torch.empty_like(dec.q))
     o_part = torch.empty((dw.batch, dw.num_qo_heads, 4, 64), dtype=torch.float32, device="cuda:0")
     lse_part = torch.empty((dw.batch, dw.num_qo_heads, 4), dtype=torch.float32, device="cuda:0")
     vo_part = torch.empty((int(vw.qo_indptr[-1]), vw.num_qo_heads, 3, 64), dtype=torch.float32, device="cuda:0")
     vlse_part = torch.empty((int(vw.qo_indptr[-1]), vw.num_qo_heads, 3), dtype=torch.float32, device="cuda:0")
+    bo_part = torch.empty((int(bw.qo_indptr[-1]), bw.num_qo_heads, 2, 64), dtype=torch.float32, device="cuda:0")
+    blse_part = torch.empty((int(bw.qo_indptr[-1]), bw.num_qo_heads, 2), dtype=torch.float32, device="cuda:0")
+    ho_part, hlse_part = torch.empty_like(o_part), torch.empty_like(lse_part)
+    ws = torch.empty(sa.decode_balanced_workspace_bytes(dw.batch, dw.num_qo_heads, 37), dtype=torch.uint8,
+                     device="cuda:0")
 
     def work(stream=None):
         sa.decode_paged(dec.q, dec.k, dec.v, dec.kv_indptr, dec.page_indices, dec.kv_len, dec.sinks, dw.scale,
@@ -46,6 +56,14 @@ def test_graph_replay_matches_eager():
         sa.decode_paged_multi(ver.q, ver.qo_indptr, ver.k, ver.v, ver.kv_indptr, ver.page_indices, ver.kv_len,
                               ver.sinks, vw.scale, 8, num_splits=3, out=outs["ver"], o_part=vo_part,
                               lse_part=vlse_part, stream=stream)
+        sa.decode_paged_multi(big.q, big.qo_indptr, big.k, big.v, big.kv_indptr, big.page_indices, big.kv_len,
+                              big.sinks, bw.scale, 8, num_splits=2, out=outs["big"], o_part=bo_part,
+                              lse_part=blse_part, stream=stream)
+        sa.decode_paged_balanced(dec.q, dec.k, dec.v, dec.kv_indptr, dec.page_indices, dec.kv_len, dec.sinks,
+                                 dw.scale, num_segments=37, out=outs["bal"], workspace=ws, stream=stream)
+        sa.decode_paged(dec.q, dec.k, dec.v, dec.kv_indptr, dec.page_indices, dec.kv_len, dec.sinks, dw.scale,
+                        num_splits=4, out=outs["host"], o_part=ho_part, lse_part=hlse_part,
+                        kv_len_host=dw.kv_len, stream=stream)
 
     work()
     torch.cuda.synchronize()

@@ -89,6 +89,19 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in p.stderr
 
 
+def test_host_order_flag():
+    """The headline's decode calls pass the host copy of kv_len unless the
+    flag asks for the kernels' own ordering."""
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        assert bench.parse().no_host_order is False
+        sys.argv = ["bench.py", "--no-host-order"]
+        assert bench.parse().no_host_order is True
+    finally:
+        sys.argv = argv
+
+
 def test_oracle_legs_cover_the_rows_they_claim():
     """The benchmark's oracle samples (sub-batches, (request, KV head)
     units, split partials) reproduce the oracle's whole-call results on the

@@ -452,6 +452,18 @@ def test_verify_host_order_is_invisible(masked):
                   f"verify host copy {name} masked={masked} S={s}")
 
 
+@pytest.mark.parametrize("window", [3, 3000])
+def test_verify_host_order_under_windows(window):
+    """Windows of at most 2048 keys leave the order to the kernels, longer
+    ones use the host order: both give the kernels' own results bit for bit."""
+    w = wl.verify_decode(batch=24)
+    d = DeviceWorkload(w)
+    say(f"verify host order window={window}")
+    base = d.decode_multi(3, 8, window=window)
+    for name, host in _host_copies(w).items():
+        _same(d.decode_multi(3, 8, window=window, kv_len_host=host), base, f"verify W={window} {name}")
+
+
 @pytest.mark.parametrize("window", [0, 128])
 def test_mixed_batch_host_order_is_invisible(window):
     w = wl.mixed_batch(n_prefill=4, chunk=200, max_prefix=900, n_decode=30, max_decode_len=1500)

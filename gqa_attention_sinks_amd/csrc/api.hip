@@ -117,6 +117,57 @@ void plan_decode_order(const sinkattn_kv* kv, int32_t batch, int32_t window, sin
   d->planned = 1;
 }
 
+// The (request, tile) of every prefill tile slot, in the order the kernel's
+// own scan gives (see kPrefillRankMaxTiles), from the caller's host copy of
+// qo_indptr (and of kv_len when the kernel would rank tiles by their key
+// counts).  The set of tiles follows qo_indptr alone; their order only sets
+// when each runs, so any copy of kv_len gives the same results.  Without key
+// counts on the host (contiguous KV), a launch that the kernel would rank
+// keeps the kernel's scan.
+bool plan_prefill_tiles(const sinkattn_kv* kv, const int32_t* qo_host, int32_t batch, int32_t window, int bm,
+                        long slots, const sinkattn::PrefillArgs& a, sinkattn::PrefillPlan* plan) {
+  using sinkattn::kPrefillPlanMax;
+  constexpr int kKeys = sinkattn::kPrefillTileKeys;
+  if (slots < 1 || slots > kPrefillPlanMax || batch > 65536) return false;
+  const bool may_rank = slots <= sinkattn::kPrefillRankMaxTiles && (window == 0 || window > sinkattn::kPlanMinWindow);
+  const int32_t* nk_host = kv->paged ? kv->kv_len_host : nullptr;
+  if (may_rank && nk_host == nullptr) return false;
+  auto n_q = [&](int32_t b) { return qo_host[b + 1] - qo_host[b]; };
+  auto n_tiles = [&](int32_t b) { return (a.skip_single_rows && n_q(b) == 1) ? 0 : (n_q(b) + bm - 1) / bm; };
+  for (int32_t b = 0; b < batch; ++b)
+    if (n_q(b) > 65535 * bm) return false;   // tile numbers must fit 16 bits
+  bool uniform = true;                 // every request shaped like request 0 (single rows included)
+  if (may_rank)
+    for (int32_t b = 1; b < batch && uniform; ++b) uniform = n_q(b) == n_q(0) && nk_host[b] == nk_host[0];
+  long r = 0;
+  if (may_rank && !uniform) {
+    // tiles request by request, then stably by decreasing key count
+    uint32_t tile_of[kPrefillPlanMax];
+    int64_t work[kPrefillPlanMax];
+    int32_t idx[kPrefillPlanMax];
+    for (int32_t b = 0; b < batch; ++b) {
+      const int64_t shift = (int64_t)nk_host[b] - n_q(b);
+      for (int32_t t = 0; t < n_tiles(b); ++t, ++r) {
+        const int64_t t0 = (int64_t)t * bm;
+        const int64_t t_last = std::min<int64_t>(t0 + bm, n_q(b)) - 1;
+        const int64_t lo_first = window > 0 ? std::max<int64_t>(0, shift + t0 - window + 1) : 0;
+        const int64_t k_first = lo_first / kKeys * kKeys;
+        work[r] = (shift + t_last + 1 - k_first + kKeys - 1) / kKeys;
+        tile_of[r] = (uint32_t)b << 16 | (uint32_t)t;
+        idx[r] = (int32_t)r;
+      }
+    }
+    std::stable_sort(idx, idx + r, [&work](int32_t x, int32_t y) { return work[x] > work[y]; });
+    for (long i = 0; i < r; ++i) plan->slot[i] = tile_of[idx[i]];
+  } else {
+    for (int32_t b = 0; b < batch; ++b) {
+      const int32_t nt = n_tiles(b);
+      for (int32_t s = 0; s < nt; ++s) plan->slot[r++] = (uint32_t)b << 16 | (uint32_t)(nt - 1 - s);
+    }
+  }
+  return r == slots;   // (always: slots counts the same tiles)
+}
+
 }  // namespace
 
 extern "C" {
@@ -174,9 +225,13 @@ sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const 
   }
   REQUIRE(slots * num_qo_heads < (1L << 31), SINKATTN_ERR_UNSUPPORTED, "launch too large");
   a.num_slots = (int32_t)slots;
+  sinkattn::PrefillPlan plan;
+  const bool planned =
+      qo_indptr_host != nullptr && plan_prefill_tiles(kv, qo_indptr_host, batch, window, bm, slots, a, &plan);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (slots > 0 && (st = hip_status(sinkattn::launch_prefill(a, total_q, s), "prefill launch")) != SINKATTN_OK)
+  if (slots > 0 &&
+      (st = hip_status(sinkattn::launch_prefill(a, planned ? &plan : nullptr, s), "prefill launch")) != SINKATTN_OK)
     return st;
   if (kv->paged && any_single) {
     sinkattn::DecodeArgs d{};

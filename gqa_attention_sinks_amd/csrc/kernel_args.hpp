@@ -52,6 +52,19 @@ struct MergeArgs {
 // Causal / sliding-window prefill: a workgroup takes one tile of query rows
 // of one query head, or of four heads of one group when the group size is a
 // multiple of four.
+// Prefill tile order: when a launch has at most kPrefillRankMaxTiles tiles,
+// its requests differ in shape and the window is unbounded or longer than
+// kPlanMinWindow keys, the tiles run in order of decreasing key count (ties
+// request by request); otherwise request by request, each request's longest
+// tile first.  A launch of at most kPrefillPlanMax tiles takes that order
+// from a plan built on the host (when the caller gives its host copies), and
+// its workgroups skip the scan that finds their tile; the plan travels as a
+// second kernel argument of its own kernel, so the other launches keep a
+// small argument block.
+constexpr int kPrefillRankMaxTiles = 256;
+constexpr int kPrefillPlanMax = 512;
+constexpr int kPrefillTileKeys = 64;        // keys per staged tile
+
 struct PrefillArgs {
   const uint16_t* q;          // [total_q, Hq, 64]
   const int32_t* qo_indptr;   // [B+1]
@@ -68,6 +81,11 @@ struct PrefillArgs {
   int32_t paged;
   int32_t skip_single_rows;   // requests with one query row are left to the decode kernel
   int32_t num_slots;          // tile slots launched (upper bound on tiles)
+};
+
+// The host plan of a prefill launch: slot[s] = request << 16 | tile.
+struct PrefillPlan {
+  uint32_t slot[kPrefillPlanMax];
 };
 
 // Balanced split decode: the batch's live pages cut into equal segments; see
@@ -124,6 +142,7 @@ hipError_t launch_merge_balanced(const BalancedArgs& a, hipStream_t stream);
 hipError_t launch_moe_topk_softmax(const MoeArgs& a, hipStream_t stream);
 hipError_t launch_append_rope(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t stream);
-hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream);
+// plan: null, or the (request, tile) of each of the a.num_slots tile slots.
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan* plan, hipStream_t stream);
 
 }  // namespace sinkattn

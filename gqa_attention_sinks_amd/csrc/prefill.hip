@@ -50,7 +50,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kRowsPerWave = 64;               // two 32-row MFMA blocks per wave
-constexpr int kBN = 64;                        // keys per tile
+constexpr int kBN = kPrefillTileKeys;          // keys per tile
 constexpr int kTileBytes = kBN * kHeadDim * 2;   // 8 KiB
 constexpr float kSumLimit = 16384.f;           // 2^14
 constexpr float kFloatMax = 3.402823466e38f;
@@ -93,19 +93,19 @@ __device__ __forceinline__ int tile_work(int n_q, int n_k, int t, int window) {
   return (shift + t_last + 1 - k_first + kBN - 1) / kBN;
 }
 
-// Under a window up to this long every query tile carries about the same
-// work (at most a few key tiles), and ranking would only cost time.
-constexpr int kRankMinWindow = 2048;
+static_assert(kPrefillRankMaxTiles == kWaves * 64, "ranking lists one tile per thread");
 
 // Find the (request, tile) handled by tile slot `slot`.  Tiles are numbered
 // request by request (every thread sums a run of requests, then a block
 // scan).  When the requests differ in shape, the batch has at most 256
-// query tiles and the window is unbounded or longer than kRankMinWindow, the
+// query tiles and the window is unbounded or longer than kPlanMinWindow, the
 // slots take the tiles in order of decreasing work (ties by number), so the
 // longest tiles of every request start first and the short ones fill the
 // tail.  Otherwise they take them request by request, longest
-// tile first: with equal requests that order is as balanced, and tiles of
-// one request that run together share its keys in L2.
+// tile first: with equal requests that order is as balanced, tiles of one
+// request that run together share its keys in L2, and under a short window
+// every tile carries about the same work (a few key tiles), so ranking would
+// only cost time.
 template <int RT>
 __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* out_b, int* out_tile) {
   constexpr int kThreads = kWaves * 64;
@@ -144,7 +144,7 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   const int total = s_scan[kThreads - 1];
   __shared__ int s_found[2];
   if (tid == 0) s_found[0] = -1;
-  if (total <= kThreads && !uniform && (a.window == 0 || a.window > kRankMinWindow)) {
+  if (total <= kThreads && !uniform && (a.window == 0 || a.window > kPlanMinWindow)) {
     // list every (request, tile) with its work, then rank
     __shared__ int s_work[kThreads];
     __shared__ int s_req[kThreads];
@@ -196,14 +196,19 @@ __device__ bool locate_tile(const PrefillArgs& a, int slot, int* s_scan, int* ou
   return s_found[0] >= 0;
 }
 
+// The second kernel argument: the host plan, or a placeholder for launches
+// whose workgroups find their tile themselves.
+template <bool PLANNED> struct PlanArg { uint32_t unused; };
+template <> struct PlanArg<true> { PrefillPlan p; };
+
 // HP: query heads per workgroup.  HP = 1: the four waves take four 64-row
 // blocks of one head (256 rows a tile).  HP = 4: they take the same 64 rows
 // of four heads that share a KV head, so every wave needs exactly the
 // workgroup's key tiles (no wave waits out another's diagonal or window
-// edge).
-template <bool PAGED, int HP>
+// edge).  PLANNED: each slot's (request, tile) comes from the host plan.
+template <bool PAGED, int HP, bool PLANNED>
 __global__ __launch_bounds__(kWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void prefill_kernel(PrefillArgs a) {
+void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
   constexpr int RT = kRowsPerWave * (kWaves / HP);   // query rows of a workgroup tile
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * 2 * kTileBytes];
   __shared__ int s_scan[kWaves * 64];
@@ -223,9 +228,15 @@ void prefill_kernel(PrefillArgs a) {
   const int head = g * a.group + hg * HP + (HP > 1 ? wave : 0);   // this wave's query head
 
   int b, tile;
-  if (!locate_tile<RT>(a, slot, s_scan, &b, &tile)) return;   // uniform over the workgroup
-  b = __builtin_amdgcn_readfirstlane(b);
-  tile = __builtin_amdgcn_readfirstlane(tile);
+  if constexpr (PLANNED) {   // every slot of a planned launch holds a tile
+    const uint32_t e = plan.p.slot[slot];
+    b = (int)(e >> 16);
+    tile = (int)(e & 0xffffu);
+  } else {
+    if (!locate_tile<RT>(a, slot, s_scan, &b, &tile)) return;   // uniform over the workgroup
+    b = __builtin_amdgcn_readfirstlane(b);
+    tile = __builtin_amdgcn_readfirstlane(tile);
+  }
 
   const int q_begin = a.qo_indptr[b];
   const int n_q = a.qo_indptr[b + 1] - q_begin;
@@ -310,33 +321,39 @@ void prefill_kernel(PrefillArgs a) {
     vr[0] = *reinterpret_cast<const u32x4*>(vbytes + base + off0);
     vr[1] = *reinterpret_cast<const u32x4*>(vbytes + base + off1);
   };
-  auto store_tile = [&](int stage, int kt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
-    uint8_t* ks = smem + stage * 2 * kTileBytes;
-    uint8_t* vs = ks + kTileBytes;
+  // Rows past the last key are staged as zeros.
+  auto fix_tail = [&](int kt, u32x4 (&kr)[2], u32x4 (&vr)[2]) {
     if (kt + kBN > n_k) {            // uniform: only the range's last tile
       __asm__ volatile("");
       if (kt + wkey + lkey >= n_k) kr[0] = vr[0] = u32x4{};
       if (kt + wkey + 8 + lkey >= n_k) kr[1] = vr[1] = u32x4{};
     }
-    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + lkey, ld_c)) = kr[0];
-    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + 8 + lkey, ld_c)) = kr[1];
-    // V is staged as fp16: the weights of the P.V product are fp16
-    u32x4 v16[2];
+  };
+  // V is staged as fp16: the weights of the P.V product are fp16.
+  auto convert_v = [&](const u32x4 (&vr)[2], u32x4 (&v16)[2]) {
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 4; ++e) v16[u][e] = bf16x2_to_f16x2(vr[u][e]);
+  };
+  auto write_tile = [&](int stage, const u32x4 (&kr)[2], const u32x4 (&v16)[2]) {
+    uint8_t* ks = smem + stage * 2 * kTileBytes;
+    uint8_t* vs = ks + kTileBytes;
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + lkey, ld_c)) = kr[0];
+    *reinterpret_cast<u32x4*>(ks + tile_swizzle(wkey + 8 + lkey, ld_c)) = kr[1];
     *reinterpret_cast<u32x4*>(vs + tile_swizzle(wkey + lkey, ld_c)) = v16[0];
     *reinterpret_cast<u32x4*>(vs + tile_swizzle(wkey + 8 + lkey, ld_c)) = v16[1];
   };
 
   int pid = 0;
   {
-    u32x4 kr[2], vr[2];
+    u32x4 kr[2], vr[2], v16[2];
     if (PAGED) pid = page_of(k_first);
     load_tile(k_first, pid, kr, vr);
     if (PAGED) pid = page_of(k_first + kBN);
-    store_tile(0, k_first, kr, vr);
+    fix_tail(k_first, kr, vr);
+    convert_v(vr, v16);
+    write_tile(0, kr, v16);
   }
   __syncthreads();
 
@@ -357,8 +374,9 @@ void prefill_kernel(PrefillArgs a) {
     constexpr int STAGE = decltype(stage_c)::value;
     constexpr uint32_t st = STAGE * 2 * kTileBytes;
     const int kt = k_first + it * kBN;
-    u32x4 kr[2], vr[2];
+    u32x4 kr[2], vr[2], v16[2];
     const bool more = it + 1 < ntiles;
+    bool converted = false;   // the next tile's V already converted (uniform)
     if (more) {
       load_tile(kt + kBN, pid, kr, vr);
       if (PAGED) pid = page_of(kt + 2 * kBN);
@@ -487,7 +505,8 @@ void prefill_kernel(PrefillArgs a) {
         }
         finish_weights(h, p0, t0s);
       }
-      if (__builtin_amdgcn_ballot_w64(t0s[0] > kSumLimit || t0s[1] > kSumLimit) != 0) rebase(0, p0, t0s);
+      if ((__builtin_amdgcn_ballot_w64(t0s[0] > kSumLimit) | __builtin_amdgcn_ballot_w64(t0s[1] > kSumLimit)) != 0)
+        rebase(0, p0, t0s);
       dsum[0] += t0s[0];
       dsum[1] += t0s[1];
       if (need_mask) mask_half(1, s1);
@@ -506,13 +525,35 @@ void prefill_kernel(PrefillArgs a) {
         }
         finish_weights(h, p1, t1s);
       }
-      if (__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit || t1s[1] > kSumLimit) != 0) rebase(1, p1, t1s);
+      if ((__builtin_amdgcn_ballot_w64(t1s[0] > kSumLimit) | __builtin_amdgcn_ballot_w64(t1s[1] > kSumLimit)) != 0)
+        rebase(1, p1, t1s);
       dsum[0] += t1s[0];
       dsum[1] += t1s[1];
-      mma_pv(v1, p1);
+      if (more) {
+        // the last product of the tile carries the conversion of the next
+        // tile's V: one dword of it after each MFMA
+        fix_tail(kt + kBN, kr, vr);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int hh = u >> 2, db = (u >> 1) & 1, rb = u & 1;
+          acc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v1[hh][db], p1[rb][hh], acc[rb][db], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          v16[u >> 2][u & 3] = bf16x2_to_f16x2(vr[u >> 2][u & 3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        converted = true;
+      } else {
+        mma_pv(v1, p1);
+      }
     }
 
-    if (more) store_tile(STAGE ^ 1, kt + kBN, kr, vr);
+    if (more) {
+      if (!converted) {
+        fix_tail(kt + kBN, kr, vr);
+        convert_v(vr, v16);
+      }
+      write_tile(STAGE ^ 1, kr, v16);
+    }
     __syncthreads();
   };
   for (int it = 0; it < ntiles; it += 2) {
@@ -550,19 +591,27 @@ void prefill_kernel(PrefillArgs a) {
 // Heads per workgroup: four when the GQA group splits into fours, else one.
 static int heads_per_workgroup(int32_t group) { return group % 4 == 0 ? 4 : 1; }
 
-hipError_t launch_prefill(const PrefillArgs& a, int32_t total_q, hipStream_t stream) {
-  (void)total_q;
+template <bool PLANNED>
+static void launch_shape(const PrefillArgs& a, const PlanArg<PLANNED>& plan, int hp, dim3 grid,
+                         hipStream_t stream) {
+  const dim3 block(kWaves * 64);
+  if (a.paged) {
+    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<true, 4, PLANNED>), grid, block, 0, stream, a, plan);
+    else hipLaunchKernelGGL((prefill_kernel<true, 1, PLANNED>), grid, block, 0, stream, a, plan);
+  } else {
+    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<false, 4, PLANNED>), grid, block, 0, stream, a, plan);
+    else hipLaunchKernelGGL((prefill_kernel<false, 1, PLANNED>), grid, block, 0, stream, a, plan);
+  }
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, const PrefillPlan* plan, hipStream_t stream) {
   const int hp = heads_per_workgroup(a.group);
   const long blocks = (long)a.num_slots * (a.num_qo_heads / hp);
   if (blocks <= 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks), block(kWaves * 64);
-  if (a.paged) {
-    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<true, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<true, 1>), grid, block, 0, stream, a);
-  } else {
-    if (hp == 4) hipLaunchKernelGGL((prefill_kernel<false, 4>), grid, block, 0, stream, a);
-    else hipLaunchKernelGGL((prefill_kernel<false, 1>), grid, block, 0, stream, a);
-  }
+  if (plan != nullptr && a.num_slots > kPrefillPlanMax) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
+  if (plan != nullptr) launch_shape<true>(a, PlanArg<true>{*plan}, hp, grid, stream);
+  else launch_shape<false>(a, PlanArg<false>{0}, hp, grid, stream);
   return hipGetLastError();
 }
 

@@ -122,10 +122,11 @@ typedef struct sinkattn_kv {
    * batch's lengths ("Accelerating Sonar through speculation", section
    * "Inference with speculative decoding": the host side of the runtime fills
    * the buffers that configure and schedule the attention kernel for each
-   * batch).  It only orders the work: the results are
-   * the same whatever it holds (the lengths the kernels use are always the
-   * device kv_len's).  sinkattn_decode_paged_balanced plans its segments on
-   * the device and does not read it. */
+   * batch).  The tile table of a paged sinkattn_prefill call also takes its
+   * order from it (see qo_indptr_host there).  It only orders the work: the
+   * results are the same whatever it holds (the lengths the kernels use are
+   * always the device kv_len's).  sinkattn_decode_paged_balanced plans its
+   * segments on the device and does not read it. */
   const int32_t* kv_len_host;
 } sinkattn_kv;
 
@@ -148,9 +149,15 @@ typedef struct sinkattn_kv {
  *              ("Accelerating Sonar through speculation", section "Inference
  *              with speculative decoding": the CPU fills the buffers that
  *              configure and schedule the attention kernel): with it the
- *              prefill grid holds exactly the query tiles of the batch;
- *              without it the grid is sized from total_q and batch and the
- *              surplus workgroups exit at once.  Results are identical. */
+ *              prefill grid holds exactly the query tiles of the batch, and
+ *              a launch of up to 512 tiles takes each workgroup's (request,
+ *              tile) from a table built here instead of a scan over the
+ *              batch in every workgroup (for a paged call that the kernel
+ *              would order by key count, the table also needs
+ *              kv->kv_len_host, which only sets the order); without it the
+ *              grid is sized from total_q and batch and the surplus
+ *              workgroups exit at once.  It must equal qo_indptr on the
+ *              device.  Results are identical either way. */
 sinkattn_status sinkattn_prefill(const void* q, const int32_t* qo_indptr, const sinkattn_kv* kv,
                                  const float* sinks, void* out, float* lse, int32_t batch,
                                  int32_t total_q, int32_t num_qo_heads, int32_t num_kv_heads,

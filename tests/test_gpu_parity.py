@@ -78,6 +78,44 @@ def test_prefill_host_plan_is_invisible(paged):
         b_out, b_lse = d.prefill(window=window, host_plan=False)
         assert np.array_equal(to_host(a_out), to_host(b_out))
         assert np.array_equal(to_host(a_lse), to_host(b_lse))
+        if paged:
+            # a tile order ranked on the host from kv_len, and one from a
+            # wrong copy of kv_len (order only): the same bits
+            for name, host in [("exact", w.kv_len), ("reversed", np.ascontiguousarray(w.kv_len[::-1]))]:
+                c_out, c_lse = d.prefill(window=window, kv_len_host=host)
+                assert np.array_equal(to_host(c_out), to_host(b_out)), name
+                assert np.array_equal(to_host(c_lse), to_host(b_lse)), name
+
+
+@pytest.mark.parametrize("case", ["rank_256", "rank_257", "plan_512", "plan_513"])
+def test_prefill_host_plan_at_its_limits(case):
+    """Launches at the limits of the host-built tile order: up to 256 tiles
+    of differently shaped requests are ranked by key count (257: request by
+    request), up to 512 tiles take their (request, tile) from the host plan
+    (513: the kernel's own scan).  Planned and unplanned launches give the
+    same bits."""
+    rng = np.random.default_rng(31)
+    if case.startswith("rank"):
+        # paged, unbounded window: 64-row tiles (16 query / 2 KV heads)
+        n = int(case.split("_")[1])
+        qo_len = np.array([64 * (n - 3), 64, 64, 64, 1, 1], dtype=np.int64)   # single rows: decode kernel
+        kv_len = qo_len + np.array([0, 3000, 10, 700, 5, 900])
+        w = wl.make_paged("rank", kv_len, qo_len, 16, 2, rng=rng)
+        windows = [0]
+        host = w.kv_len
+    else:
+        # contiguous, 128-key window (no ranking): 512 tiles, or 513 with one more row
+        qo_len = np.array([64 * 256, 64 * 256] + ([1] if case == "plan_513" else []), dtype=np.int64)
+        w = wl.make_contiguous("plan", qo_len, qo_len, 16, 2, rng=rng)
+        windows = [128]
+        host = None
+    say(f"prefill host plan limit {case}: qo={list(qo_len)}")
+    d = DeviceWorkload(w)
+    for window in windows:
+        a_out, a_lse = d.prefill(window=window, kv_len_host=host)
+        b_out, b_lse = d.prefill(window=window, host_plan=False)
+        assert np.array_equal(to_host(a_out), to_host(b_out))
+        assert np.array_equal(to_host(a_lse), to_host(b_lse))
 
 
 @pytest.mark.parametrize("group", [1, 4, 16])

@@ -122,8 +122,8 @@ void plan_decode_order(const sinkattn_kv* kv, int32_t batch, int32_t window, sin
 // qo_indptr (and of kv_len when the kernel would rank tiles by their key
 // counts).  The set of tiles follows qo_indptr alone; their order only sets
 // when each runs, so any copy of kv_len gives the same results.  Without key
-// counts on the host (contiguous KV), a launch that the kernel would rank
-// keeps the kernel's scan.
+// counts on the host (contiguous KV), a launch of several requests that the
+// kernel would rank keeps the kernel's scan.
 bool plan_prefill_tiles(const sinkattn_kv* kv, const int32_t* qo_host, int32_t batch, int32_t window, int bm,
                         long slots, const sinkattn::PrefillArgs& a, sinkattn::PrefillPlan* plan) {
   using sinkattn::kPrefillPlanMax;
@@ -131,7 +131,7 @@ bool plan_prefill_tiles(const sinkattn_kv* kv, const int32_t* qo_host, int32_t b
   if (slots < 1 || slots > kPrefillPlanMax || batch > 65536) return false;
   const bool may_rank = slots <= sinkattn::kPrefillRankMaxTiles && (window == 0 || window > sinkattn::kPlanMinWindow);
   const int32_t* nk_host = kv->paged ? kv->kv_len_host : nullptr;
-  if (may_rank && nk_host == nullptr) return false;
+  if (may_rank && nk_host == nullptr && batch > 1) return false;   // one request: nothing to rank
   auto n_q = [&](int32_t b) { return qo_host[b + 1] - qo_host[b]; };
   auto n_tiles = [&](int32_t b) { return (a.skip_single_rows && n_q(b) == 1) ? 0 : (n_q(b) + bm - 1) / bm; };
   for (int32_t b = 0; b < batch; ++b)

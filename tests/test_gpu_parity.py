@@ -87,15 +87,21 @@ def test_prefill_host_plan_is_invisible(paged):
                 assert np.array_equal(to_host(c_lse), to_host(b_lse)), name
 
 
-@pytest.mark.parametrize("case", ["rank_256", "rank_257", "plan_512", "plan_513"])
+@pytest.mark.parametrize("case", ["rank_256", "rank_257", "plan_512", "plan_513", "one_request"])
 def test_prefill_host_plan_at_its_limits(case):
     """Launches at the limits of the host-built tile order: up to 256 tiles
     of differently shaped requests are ranked by key count (257: request by
     request), up to 512 tiles take their (request, tile) from the host plan
-    (513: the kernel's own scan).  Planned and unplanned launches give the
-    same bits."""
+    (513: the kernel's own scan); a single request over contiguous KV is
+    planned with no key counts on the host (nothing to rank).  Planned and
+    unplanned launches give the same bits."""
     rng = np.random.default_rng(31)
-    if case.startswith("rank"):
+    if case == "one_request":
+        qo_len = np.array([300], dtype=np.int64)
+        w = wl.make_contiguous("one", np.array([1000]), qo_len, 16, 2, rng=rng)
+        windows = [0, 128]
+        host = None
+    elif case.startswith("rank"):
         # paged, unbounded window: 64-row tiles (16 query / 2 KV heads)
         n = int(case.split("_")[1])
         qo_len = np.array([64 * (n - 3), 64, 64, 64, 1, 1], dtype=np.int64)   # single rows: decode kernel

@@ -190,6 +190,10 @@ void decode_paged_kernel(DecodeArgs a) {
   };
   load_page(wp0);
 
+  // Waves streaming pages issue ahead of waves of other workgroups that are
+  // loading their queries or merging their results (the loop is the part
+  // whose loads must stay in flight).
+  __builtin_amdgcn_s_setprio(3);
   for (int p = wp0; p < wp1; ++p) {
     // scores of page p
     f32x4 sc = {};
@@ -263,6 +267,7 @@ void decode_paged_kernel(DecodeArgs a) {
   float* sm_m = reinterpret_cast<float*>(smem);
   float* sm_d = sm_m + NW * 16;
   float* sm_o = sm_d + NW * 16;   // [NW][16 columns][64 dims]
+  __builtin_amdgcn_s_setprio(0);
   __syncthreads();                // the staging area is free
   if (grp == 0) {
     sm_m[wave * 16 + col] = m;
@@ -330,8 +335,7 @@ __device__ __forceinline__ void merge_regs(const float* lp, const float* op, int
   }
   if (mx == kNegInf) return;
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if (c >= S) break;
+  for (int c = 0; c < N; ++c) {   // chunks past S - 1 weigh exp2(-inf) = 0
     const float wt = (l[c] == mx) ? 1.f : exp2_hw((l[c] - mx) * kLog2e);
     den += wt;
     num += wt * o[c];
@@ -391,8 +395,8 @@ __device__ __forceinline__ void merge_regs4(const float* lp, const f32x4* op, in
   }
   if (mx == kNegInf) return;
 #pragma unroll
-  for (int c = 0; c < N; ++c) {
-    if (c >= S) break;
+  for (int c = 0; c < N; ++c) {   // chunks past S - 1 weigh exp2(-inf) = 0 (no early exit:
+                                  // the partials stay in registers)
     const float wt = (l[c] == mx) ? 1.f : exp2_hw((l[c] - mx) * kLog2e);
     den += wt;
 #pragma unroll

@@ -1,7 +1,8 @@
 """Every kernel instantiation compiles for gfx950 without register spills
-(a spill turns into scratch-memory traffic inside the hot loops) and within
-the LDS of one workgroup.  Compiles each kernel source to assembly with the
-library's own flags; no GPU needed."""
+and without any other scratch memory (a spill, or a local array the compiler
+cannot keep in registers, turns into memory traffic inside the hot loops),
+and within the LDS of one workgroup.  Compiles each kernel source to
+assembly with the library's own flags; no GPU needed."""
 
 import os
 import re
@@ -32,5 +33,7 @@ def test_no_spills_and_lds_fits(src):
         vspill = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1))
         sspill = int(re.search(r"\.sgpr_spill_count:\s+(\d+)", block).group(1))
         lds = int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1))
+        scratch = int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1))
         assert vspill == 0 and sspill == 0, f"{name}: {vspill} VGPR / {sspill} SGPR spills"
+        assert scratch == 0, f"{name}: {scratch} bytes of scratch per lane"
         assert lds <= 160 * 1024, f"{name}: {lds} bytes of LDS"

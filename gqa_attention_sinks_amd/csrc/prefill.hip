@@ -280,6 +280,8 @@ void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
   // accumulator.  The sink is folded in at the end (fold_sink), which yields
   // the state of the sink-seeded recurrence.
   float m[2] = {-kFloatMax, -kFloatMax}, dsum[2] = {0.f, 0.f};
+  // the head's sink, loaded now so that its latency is not paid at the end
+  const float sink2 = a.sinks != nullptr ? a.sinks[head] * kLog2e : kNegInf;
   f32x16 acc[2][2] = {};   // [row block][dim block]
   const float c = a.scale_log2;
   const TileLanes tl = tile_lanes(lane);
@@ -484,6 +486,21 @@ void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
       mma_scores(k0, s0);
       reads_then_mfmas<8, 8>();
       if (need_mask) mask_half(0, s0);
+      if (it == 0) {
+        // the launch's first tile: the reference goes to the row maxima of
+        // its first half before any weight is taken (from -FLT_MAX every
+        // weight would overflow and the half be redone); acc and the
+        // denominator are still zero, so nothing is rescaled
+        __asm__ volatile("");
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          float mx = s0[rb][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s0[rb][i]);
+          mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+          m[rb] = fmaxf(m[rb], mx * c);
+        }
+      }
       // The two overlapped steps are interleaved by hand: each MFMA is
       // followed by four weights of the other half (fma, exp2, pack), and
       // scheduling fences keep the compiler from regrouping them, so the
@@ -562,7 +579,6 @@ void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
   }
 
   if (!wave_live) return;
-  const float sink2 = a.sinks != nullptr ? a.sinks[head] * kLog2e : kNegInf;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     const float d = dsum[rb] + shfl_xor_f32(dsum[rb], 32);

@@ -34,8 +34,10 @@
 //   against the current reference, and only if some lane's share of a row's
 //   weight sum exceeds 2^14 (a key far above the reference; fp16 weights stay
 //   finite below 65504) does the wave find the tile's row maxima, move the
-//   reference up, rescale and recompute.  A row's first tile always does (the
-//   reference starts at -FLT_MAX), later ones almost never.
+//   reference up, rescale and recompute.  A workgroup's first key tile
+//   instead takes the reference from the row maxima of its first half
+//   before any weight (it starts at -FLT_MAX); later tiles almost never
+//   move it.
 //   Masking is applied only on tiles that cross the causal diagonal or the
 //   window's lower edge.
 
@@ -445,7 +447,7 @@ void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
             acc[1][db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vt[hh][db], pop[1][hh], acc[1][db], 0, 0, 0);
           }
       };
-      // rare path of a half (always on a row's first tile): recompute its
+      // rare path of a half (a key far above the reference): recompute its
       // scores from the staged tile, move the reference to the row maxima,
       // rescale, and redo the weights
       auto rebase = [&](int kb, f16x8 (&pop)[2][2], float (&tsum)[2]) {
@@ -487,10 +489,10 @@ void prefill_kernel(PrefillArgs a, PlanArg<PLANNED> plan) {
       reads_then_mfmas<8, 8>();
       if (need_mask) mask_half(0, s0);
       if (it == 0) {
-        // the launch's first tile: the reference goes to the row maxima of
-        // its first half before any weight is taken (from -FLT_MAX every
-        // weight would overflow and the half be redone); acc and the
-        // denominator are still zero, so nothing is rescaled
+        // the workgroup's first key tile: the reference goes to the row
+        // maxima of its first half before any weight is taken (from
+        // -FLT_MAX every weight would overflow and the half be redone);
+        // acc and the denominator are still zero, so nothing is rescaled
         __asm__ volatile("");
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {

@@ -139,6 +139,21 @@ def test_prefill_group_sizes_and_no_sinks(group):
     assert_parity(to_host(out), ro, f"prefill group {group} no sinks", to_host(lse), rl)
 
 
+@pytest.mark.parametrize("window", [37, 100])
+@pytest.mark.parametrize("group", [1, 2, 8])
+def test_prefill_group_sizes_under_windows(group, window):
+    """Groups that do not split into fours put 256 consecutive rows of one
+    head in a workgroup: under a window the later waves skip the
+    workgroup's first key tiles and meet their first visible keys later."""
+    rng = np.random.default_rng(40 + group + window)
+    hkv = 2
+    w = wl.make_paged("groups_w", [700, 90], [600, 90], hkv * group, hkv, rng=rng)
+    say(f"prefill group={group} window={window}")
+    out, lse = DeviceWorkload(w).prefill(window=window)
+    ro, rl = oracle_full(w, window)
+    assert_parity(to_host(out), ro, f"prefill group {group} window {window}", to_host(lse), rl)
+
+
 def test_prefill_outlier_sinks():
     rng = np.random.default_rng(13)
     w = wl.make_paged("outliers", [300, 64], [300, 64], 16, 2, rng=rng, sink_overrides=wl.outlier_sinks)

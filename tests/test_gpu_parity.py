@@ -107,7 +107,7 @@ def test_prefill_host_plan_at_its_limits(case):
         qo_len = np.array([64 * (n - 3), 64, 64, 64, 1, 1], dtype=np.int64)   # single rows: decode kernel
         kv_len = qo_len + np.array([0, 3000, 10, 700, 5, 900])
         w = wl.make_paged("rank", kv_len, qo_len, 16, 2, rng=rng)
-        windows = [0]
+        windows = [0, 3000]   # ranked also under a window longer than 2048 keys
         host = w.kv_len
     else:
         # contiguous, 128-key window (no ranking): 512 tiles, or 513 with one more row

@@ -102,6 +102,27 @@ def test_append_rope_shapes(interleaved, heads):
     say(f"append heads={heads} interleaved={interleaved}: {n} tokens")
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_append_random_shapes(seed):
+    """Seeded random batches: head counts, requests, prefix lengths (also
+    page-aligned and empty prefixes), new-token counts, pair layout, queries
+    rotated in place, kept apart or not given, and a table that may end
+    before the last positions."""
+    rng = np.random.default_rng(500 + seed)
+    hq, hkv = [(64, 8), (8, 8), (16, 2), (4, 1), (32, 4)][rng.integers(5)]
+    batch = int(rng.integers(1, 12))
+    n_new = rng.integers(1, 70, size=batch)
+    prefix = rng.choice([0, 16, 32, 15, 17, 100, 1000, 4095], size=batch)
+    kv_len = prefix + n_new
+    max_pos = int(kv_len.max()) + 1 if rng.random() < 0.7 else int(rng.integers(1, kv_len.max() + 1))
+    c = _case(600 + seed, kv_len, n_new, hq, hkv, max_pos=max_pos)
+    interleaved = bool(rng.integers(2))
+    mode = int(rng.integers(3))   # 0: queries out of place, 1: in place, 2: keys only
+    n = _check(c, interleaved, with_q=mode != 2, in_place=mode == 1)
+    say(f"append random seed={seed}: B={batch} H={hq}/{hkv} interleaved={interleaved} mode={mode} "
+        f"table={max_pos}: {n} tokens placed")
+
+
 def test_append_in_place_keys_only_and_out_of_table():
     c = _case(7, [33, 100, 64], [3, 5, 2], 64, 8, max_pos=98)   # request 1's last two positions are past the table
     _check(c, False, in_place=True)
